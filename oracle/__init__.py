@@ -1,0 +1,42 @@
+"""fp64 CPU oracle for rotated-int8 ("kvi8r") K/V quantisation and chunked attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call, link or
+run anything in this package: only the tests, the package smoke check and the
+bench's CPU-baseline leg use it.  It shares no code with the HIP kernels or the
+C-ABI library and imports nothing from them.
+
+It is plain and slow on purpose: explicit matrices instead of butterflies,
+fp64 NumPy throughout, per-head processing.  What it follows:
+
+* "H3 Streamed Blocks (exact low-VRAM, alpha)" node page, Inputs table,
+  kv_store row: K and V held as int8 with one fp16 scale per (token, head) row
+  in a fixed orthonormal 128-wide Hadamard-rotated basis; the query chunk is
+  rotated to match and the output un-rotated once; a block dequant is one
+  int8 -> fp16 cast times the scale; attention runs blockwise (kv_block) with an
+  online-softmax combine.  Same row: q_chunk "exact at any value".
+* "Low VRAM, low RAM: the de-rope on a 16 GB card" page, "The K/V store
+  options": scores are invariant under the rotation, P.V is brought back
+  through the transpose once; fp16 rather than bf16 inside kvi8r.
+* "H3-Optimizations" page, Nodes (H3 Sparse Attention and the routed-geometry
+  paragraph): 64Q x 64KV tiles, the hard arm drops rejected tiles.
+
+Modules: ``hadamard`` (the basis), ``encodings`` (exact bf16/fp16 decoding and
+fp16 rounding), ``kvi8r`` (quantise / dequantise), ``attention`` (exact, kvi8r,
+tile-masked and blockwise log-sum-exp attention).
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, invariants, brute force and an independent library
+routine; none is "parity unpinned".
+"""
+from .hadamard import sylvester_hadamard, orthonormal_hadamard
+from .encodings import bf16_to_f64, f16_to_f64, f64_to_f16_bits
+from .kvi8r import rotate_rows, row_scales, codes_for_scales, quantize_rows, dequantize_rows
+from .attention import (attention, attention_blockwise, kvi8r_attention, expand_tile_mask,
+                        exact_attention_bf16)
+
+__all__ = [
+    "sylvester_hadamard", "orthonormal_hadamard", "bf16_to_f64", "f16_to_f64", "f64_to_f16_bits",
+    "rotate_rows", "row_scales", "codes_for_scales", "quantize_rows", "dequantize_rows",
+    "attention", "attention_blockwise", "kvi8r_attention", "expand_tile_mask",
+    "exact_attention_bf16",
+]
