@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the kvi8r / exact chunked-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input at
+217088 tokens x 32 heads x 128 dims (q_chunk = kv_chunk = kv_block = 16384):
+  1. build the kvi8r store: h3a_kv_quantize over K and V, one call per kv_chunk;
+  2. kvi8r attention: h3a_attention (rotate each query chunk, attention over the
+     int8 store dequantised in the loop, un-rotate once);
+  3. exact attention: h3a_attention on the bf16 store.
+Inputs are resident in HBM before timing.  `value` is the algorithmic attention
+throughput of the step, 2 x 4*S*S*H*128 flop over the step's wall time.
+
+Prints one JSON line.  Only one GPU is supported; --gpus N with N > 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_inputs(w):
+    import numpy as np
+    import torch
+
+    import synth
+
+    out = {t: torch.empty((w.seq, w.heads, 128), dtype=torch.bfloat16, device="cuda") for t in ("q", "k", "v")}
+    lock = threading.Lock()
+
+    def sink(t, h, bits):
+        src = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+        with lock:
+            out[t][:, h, :].copy_(src)
+            torch.cuda.synchronize()
+
+    synth.for_each_head(w, ("q", "k", "v"), sink)
+    return out
+
+
+def attention_flops(w, mask=None) -> float:
+    """Algorithmic flops of one attention pass: 4 * 128 per (query, kept key) pair."""
+    if mask is None:
+        return 4.0 * w.seq * w.seq * w.heads * 128
+    import numpy as np
+
+    t = 64
+    nt = w.n_tiles
+    rows = np.full(nt, t, dtype=np.float64)
+    rows[-1] = w.seq - t * (nt - 1)
+    keys = rows.copy()
+    return float(4.0 * 128 * np.einsum("hqk,q,k->", mask.astype(np.float64), rows, keys))
+
+
+def cpu_baseline(w, store, seconds: float):
+    """The fp64 oracle on a bounded sample: kvi8r attention of head 0 rows against the full store."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        cores = len(os.sched_getaffinity(0))
+    kc, vc, sc = store
+    host = lambda t: t.cpu().contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+    kcodes, ks = kc[0].cpu().numpy(), host(sc[0, 0])
+    vcodes, vs = vc[0].cpu().numpy(), host(sc[1, 0])
+    q = oracle.bf16_to_f64(synth.head_bf16(w, "q", 0))
+    scale = 1.0 / math.sqrt(128)
+    block = 256
+    rows = 0
+    t0 = time.perf_counter()
+    while True:
+        r0 = (rows * 7919) % (w.seq - block)
+        oracle.kvi8r_attention(q[r0:r0 + block], kcodes, ks, vcodes, vs, scale)
+        rows += block
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    flops = 4.0 * rows * w.seq * 128
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"kvi8r attention (fp64 NumPy oracle) of {rows} query rows of head 0 against all "
+                      f"{w.seq} keys, in blocks of {block} rows, {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="long217k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the path shards by heads with no exchange, see the design notes", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import store_kvi8r_quantize_amd as h3a
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if w.sparse:
+        raise SystemExit("bench.py times the dense long-sequence workload; sparse workloads are parity cases")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"generating {w.name}: S={w.seq} H={w.heads}")
+    t_gen = time.time()
+    x = make_inputs(w)
+    log(f"inputs resident in {time.time() - t_gen:.1f} s")
+    kc, vc, sc = h3a.new_kvi8r_store(w.seq, w.heads, device=dev)
+    out_r = torch.empty_like(x["q"])
+    out_e = torch.empty_like(x["q"])
+    ws_bytes = max(h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, w.q_chunk, m, False)
+                   for m in ("kvi8r", "exact"))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ev = {k: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for k in ("quant", "kvi8r", "exact")}
+    acc_ms = {k: 0.0 for k in ev}
+
+    def step(record: bool):
+        if record:
+            ev["quant"][0].record(stream)
+        for t0 in range(0, w.seq, w.q_chunk):
+            h3a.h3a_kv_quantize(x["k"][t0:t0 + w.q_chunk], kc, sc[0], token_offset=t0)
+            h3a.h3a_kv_quantize(x["v"][t0:t0 + w.q_chunk], vc, sc[1], token_offset=t0)
+        if record:
+            ev["quant"][1].record(stream)
+            ev["kvi8r"][0].record(stream)
+        h3a.h3a_attention(x["q"], kc, vc, sc, out_r, q_chunk=w.q_chunk, kv_block=w.kv_block, mode="kvi8r",
+                          workspace=ws)
+        if record:
+            ev["kvi8r"][1].record(stream)
+            ev["exact"][0].record(stream)
+        h3a.h3a_timing_enable(False)
+        h3a.h3a_attention(x["q"], x["k"], x["v"], None, out_e, q_chunk=w.q_chunk, kv_block=w.kv_block,
+                          mode="exact", workspace=ws)
+        if record:
+            ev["exact"][1].record(stream)
+
+    for i in range(args.warmup):
+        step(False)
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
+
+    # Timed region: K steps between two device synchronisations.  Attention-kernel
+    # launches of the kvi8r pass are bracketed by library-side HIP events.
+    kern_ms, kern_n = 0.0, 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        h3a.h3a_timing_enable(True)
+        step(True)
+        h3a.h3a_timing_enable(False)
+        torch.cuda.synchronize()
+        for k in ev:
+            acc_ms[k] += ev[k][0].elapsed_time(ev[k][1])
+        ms, n = h3a.h3a_timing_collect()
+        kern_ms += ms
+        kern_n += n
+        log(f"step {i + 1}/{args.steps}: kvi8r {ev['kvi8r'][0].elapsed_time(ev['kvi8r'][1]):.1f} ms, "
+            f"exact {ev['exact'][0].elapsed_time(ev['exact'][1]):.1f} ms")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1000.0 / args.steps
+
+    f_mode = attention_flops(w)
+    tflops = 2 * f_mode / (ms_step / 1000.0) / 1e12
+    per = {k: acc_ms[k] / args.steps for k in acc_ms}
+    kern_avg_ms = kern_ms / max(kern_n, 1)
+    flops_per_launch = f_mode * args.steps / max(kern_n, 1)
+    achieved = flops_per_launch / (kern_avg_ms / 1000.0) / 1e12
+    quant_bytes = 2.0 * w.seq * w.heads * (256 + 128 + 2)
+    res = {
+        "metric": "attention TFLOP/s at 217k tok, 32h x 128d (kvi8r/exact); % fp16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16+bf16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "seq": w.seq, "heads": w.heads, "head_dim": 128, "q_chunk": w.q_chunk,
+                   "kv_chunk": w.q_chunk, "kv_block": w.kv_block, "modes": ["kvi8r", "exact"],
+                   "step": "kv_quantize(K,V) + attention(kvi8r) + attention(exact)"},
+        "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
+        "phases_ms": {k: round(v, 3) for k, v in per.items()},
+        "modes": {
+            "kvi8r": {"tflops": round(f_mode / (per["kvi8r"] / 1000) / 1e12, 2),
+                      "frac_of_peak": round(f_mode / (per["kvi8r"] / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4)},
+            "exact": {"tflops": round(f_mode / (per["exact"] / 1000) / 1e12, 2),
+                      "frac_of_peak": round(f_mode / (per["exact"] / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4)},
+        },
+        "kv_quantize": {"ms": round(per["quant"], 3), "GB_per_s": round(quant_bytes / (per["quant"] / 1000) / 1e9, 1),
+                        "frac_of_hbm_peak": round(quant_bytes / (per["quant"] / 1000) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "roofline": {"kernel": "attn_fwd_kernel<1,8,false> (kvi8r dense)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                     "launches_per_step": kern_n // args.steps, "avg_launch_ms": round(kern_avg_ms, 3),
+                     "flops_per_launch": flops_per_launch},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(w, (kc, vc, sc), args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

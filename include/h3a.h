@@ -1,0 +1,166 @@
+/*
+ * h3a.h -- C ABI of the rotated-int8 ("kvi8r") K/V store and token-chunked
+ * long-sequence attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute follows three pages:
+ *   [P1] "H3 Streamed Blocks (exact low-VRAM, alpha)" node page:
+ *        "How it works" and the Inputs table (rows q_chunk, kv_chunk, kv_block,
+ *        kv_store).
+ *   [P2] "Low VRAM, low RAM: the de-rope on a 16 GB card" page:
+ *        "The K/V store options" (table and rotation paragraph) and
+ *        "What is exact, and what is not".
+ *   [P3] "H3-Optimizations" extension page: "Nodes" (H3 Sparse Attention,
+ *        H3 Sparse Attention (Advanced) and the routed-geometry paragraph).
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is device memory owned by the caller, and must stay
+ *     valid until the work queued on `stream` has finished.  The library keeps
+ *     no pointer after a call returns and allocates no device memory; scratch
+ *     space comes only through the `workspace` argument.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     GPU work is queued asynchronously on it, in call order.
+ *   - Arguments are checked before anything is queued.  A failed check returns
+ *     a negative status, queues nothing, and leaves a one-line reason in
+ *     h3a_last_error().  Device pointers are checked to lie inside one device
+ *     allocation large enough for the access the call will make.
+ *   - No fallback: a request the library cannot serve is an error, never a
+ *     silent substitute [P3, Nodes: explicit selections are hard requirements].
+ *   - head_dim must be 128: the width of the fixed Hadamard basis [P1 kv_store].
+ *   - Token-major tensors are [tokens, n_heads, 128] with the 128 values of a
+ *     (token, head) row contiguous.
+ */
+#ifndef H3A_H
+#define H3A_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H3A_ABI_VERSION 1
+#define H3A_HEAD_DIM 128
+#define H3A_TILE 64 /* 64Q x 64KV routing granularity [P3] */
+
+/* Status codes. */
+#define H3A_OK 0
+#define H3A_EINVAL (-1)       /* an argument is out of range, null, misaligned or too small */
+#define H3A_EUNSUPPORTED (-2) /* a valid request this library does not implement (e.g. head_dim != 128) */
+#define H3A_EHIP (-3)         /* the HIP runtime reported an error (text in h3a_last_error) */
+#define H3A_EWORKSPACE (-4)   /* workspace missing or smaller than h3a_attention_workspace_bytes */
+
+/* K/V store kinds, named after the kv_store choices they implement [P1 kv_store]. */
+#define H3A_MODE_EXACT_BF16 0 /* "bf16 (exact)": K/V kept as bf16, stock attention math */
+#define H3A_MODE_KVI8R 1      /* "kvi8r": rotated int8 K/V with one fp16 scale per (token, head) row */
+
+/* ABI version of the loaded library; callers compare it with H3A_ABI_VERSION. */
+int32_t h3a_abi_version(void);
+
+/* One line describing the last failed check on the calling thread ("" if none). */
+const char* h3a_last_error(void);
+
+/*
+ * h3a_kv_quantize -- build one kv_chunk of the kvi8r store [P1 kv_chunk, kv_store].
+ *
+ * For every (token, head) row x of the chunk (128 bf16 values):
+ *   y = x H, H the orthonormal 128x128 Sylvester Hadamard basis (natural order,
+ *     entries +-1/sqrt(128));
+ *   scale = fp16(max|y| / 127), rounded to nearest-even from the exact value;
+ *     0 for a zero row; saturates at 65504;
+ *   code_i = clamp(round-half-even(y_i / scale), -127, 127) as int8, taken in
+ *     fp32 against the stored (rounded) scale.
+ *
+ * x:               bf16 [n_tokens, n_heads, 128]; token t, head h starts at
+ *                  element t * x_token_stride + h * 128.  16-byte aligned.
+ * x_token_stride:  elements between consecutive tokens; >= n_heads * 128 and a
+ *                  multiple of 8 (so a slice of a fused QKV buffer can be passed).
+ * token_offset:    first store row written; token_offset + n_tokens <= s_total.
+ * s_total:         rows per head of the whole store.
+ * codes:           int8  [n_heads, s_total, 128] (head-major), 16-byte aligned.
+ * scales_f16:      fp16  [n_heads, s_total] (head-major), 2-byte aligned.
+ * Rows [token_offset, token_offset + n_tokens) of every head are written;
+ * nothing else is touched, so a store can be built chunk by chunk and the
+ * result equals one call over all tokens.  n_tokens == 0 is a no-op.
+ * Inputs must be finite (a non-finite row gets unspecified codes and scale).
+ */
+int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads,
+                        int32_t head_dim, int64_t token_offset, int64_t s_total, int8_t* codes,
+                        void* scales_f16, void* stream);
+
+/*
+ * h3a_attention_workspace_bytes -- bytes of workspace h3a_attention needs.
+ * sparse != 0 when a tile_mask will be passed.  Returns 0 when none is needed.
+ */
+size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim,
+                                     int64_t q_chunk, int32_t mode, int32_t sparse);
+
+/*
+ * h3a_attention -- token-chunked full (non-causal) attention of every head
+ * against a whole-sequence K/V store [P1 "How it works", q_chunk, kv_block,
+ * kv_store; P2 "The K/V store options"; P3 Nodes for tile_mask].
+ *
+ *   O[t, h, :] = sum_j softmax_j(softmax_scale * q[t,h,:] . k[j,h,:]) v[j,h,:]
+ *
+ * mode H3A_MODE_EXACT_BF16: k_store / v_store are bf16 [s_kv, n_heads, 128]
+ *   (token-major), scales must be NULL.  Inputs feed bf16 matrix cores, fp32
+ *   accumulation.  The output is bitwise identical for every q_chunk and
+ *   kv_block (each row's arithmetic depends only on s_kv).
+ * mode H3A_MODE_KVI8R: k_store / v_store are the int8 codes [n_heads, s_kv, 128]
+ *   written by h3a_kv_quantize, scales is fp16 [2, n_heads, s_kv] (K scales,
+ *   then V scales).  Each query chunk is rotated into the Hadamard basis
+ *   (rounded to fp16), attends the K/V rows dequantised on the fly as one
+ *   int8 -> fp16 cast times the row scale, with fp16 matrix-core products and
+ *   fp32 accumulation, and the output is rotated back once per row.
+ *
+ * q:          bf16 [s_q, n_heads, 128], 16-byte aligned.
+ * out:        bf16 [s_q, n_heads, 128], 16-byte aligned; must not alias inputs.
+ * q_chunk:    query tokens per pass (>= 1; a multiple of 64 when tile_mask is
+ *             given).  Query chunks are attended one after another on `stream`.
+ * kv_block:   K/V block length of the online-softmax (log-sum-exp) combine:
+ *             0 (mode default) or a positive multiple of 64.  The softmax state
+ *             is carried in registers across blocks, so the result does not
+ *             depend on it.
+ * tile_mask:  NULL for dense attention, else uint8 [n_heads, ceil(s_q/64),
+ *             ceil(s_kv/64)]: entry != 0 keeps the 64-query x 64-key tile, 0
+ *             drops it from the softmax (hard arm).  A query row with no kept
+ *             key gets an all-zero output, as does every row when s_kv == 0.
+ * workspace:  at least h3a_attention_workspace_bytes(...) bytes of device
+ *             memory, 256-byte aligned (may be NULL when that is 0).
+ */
+int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, const void* scales,
+                      int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                      int64_t q_chunk, int64_t kv_block, int32_t mode, const uint8_t* tile_mask,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * h3a_rotate_rows -- y = fp16(x H) for n_rows rows of 128 bf16 values (the
+ * query rotation of the kvi8r mode [P1 kv_store]; the same kernel that
+ * h3a_attention runs).  x bf16 [n_rows, 128], y fp16 [n_rows, 128], both
+ * 16-byte aligned.
+ */
+int32_t h3a_rotate_rows(const void* x_bf16, void* y_f16, int64_t n_rows, void* stream);
+
+/*
+ * h3a_unrotate_rows -- y = bf16(x H^T) for n_rows rows of 128 fp32 values (the
+ * single output un-rotation of the kvi8r mode [P2, rotation paragraph]; the
+ * same kernel that h3a_attention runs).  x fp32 [n_rows, 128], y bf16
+ * [n_rows, 128], both 16-byte aligned.
+ */
+int32_t h3a_unrotate_rows(const float* x_f32, void* y_bf16, int64_t n_rows, void* stream);
+
+/*
+ * Kernel timing for measurement.  While enabled, h3a_attention brackets every
+ * launch of its attention kernel with a pair of HIP events recorded on the
+ * call's stream.  h3a_timing_collect waits for the recorded events, returns the
+ * summed kernel time (ms) and the number of launches since the last collect,
+ * and clears the record.  Disabled by default.
+ */
+int32_t h3a_timing_enable(int32_t on);
+int32_t h3a_timing_collect(double* attn_ms, int64_t* attn_launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H3A_H */

@@ -1,0 +1,214 @@
+"""Python binding of libh3a.so: rotated-int8 ("kvi8r") K/V store and chunked attention on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/h3a.h.  Tensors are PyTorch
+device tensors (PyTorch provides device memory and streams); the functions
+pass their device pointers, shapes and the current HIP stream to the library.
+There is no CPU fallback: if the library is not built, or its ABI version does
+not match, every call raises.
+
+Functions carry the C names: h3a_kv_quantize, h3a_attention,
+h3a_attention_workspace_bytes, h3a_rotate_rows, h3a_unrotate_rows,
+h3a_timing_enable, h3a_timing_collect, h3a_abi_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+ABI_VERSION = 1
+HEAD_DIM = 128
+TILE = 64
+MODE_EXACT_BF16 = 0
+MODE_KVI8R = 1
+MODES = {"exact": MODE_EXACT_BF16, "bf16": MODE_EXACT_BF16, "kvi8r": MODE_KVI8R}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libh3a.so")
+
+_lib = None
+
+
+class H3AError(RuntimeError):
+    """A call into libh3a returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"h3a status {status}: {message}")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m store_kvi8r_quantize_amd.build` "
+                           "(or __graft_entry__.build()) first")
+    # torch is imported above, so its HIP runtime is already mapped and the
+    # library binds to that same runtime (one HIP runtime per process).
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.h3a_abi_version.restype = i32
+    lib.h3a_abi_version.argtypes = []
+    lib.h3a_last_error.restype = ctypes.c_char_p
+    lib.h3a_last_error.argtypes = []
+    lib.h3a_kv_quantize.restype = i32
+    lib.h3a_kv_quantize.argtypes = [vp, i64, i64, i32, i32, i64, i64, vp, vp, vp]
+    lib.h3a_attention_workspace_bytes.restype = sz
+    lib.h3a_attention_workspace_bytes.argtypes = [i64, i64, i32, i32, i64, i32, i32]
+    lib.h3a_attention.restype = i32
+    lib.h3a_attention.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64, i32, vp, vp, vp, sz, vp]
+    lib.h3a_rotate_rows.restype = i32
+    lib.h3a_rotate_rows.argtypes = [vp, vp, i64, vp]
+    lib.h3a_unrotate_rows.restype = i32
+    lib.h3a_unrotate_rows.argtypes = [vp, vp, i64, vp]
+    lib.h3a_timing_enable.restype = i32
+    lib.h3a_timing_enable.argtypes = [i32]
+    lib.h3a_timing_collect.restype = i32
+    lib.h3a_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    if lib.h3a_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"libh3a ABI {lib.h3a_abi_version()} != binding ABI {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _load()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise H3AError(rc, _lib.h3a_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t, name, dtype):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def h3a_abi_version() -> int:
+    return _load().h3a_abi_version()
+
+
+def h3a_kv_quantize(x, codes, scales, token_offset: int = 0, stream=None):
+    """Quantise x (bf16 [n_tokens, n_heads, 128], rows contiguous) into rows
+    [token_offset, token_offset + n_tokens) of a kvi8r store: codes int8
+    [n_heads, s_total, 128] and scales fp16 [n_heads, s_total]."""
+    lib = _load()
+    _need(x, "x", torch.bfloat16)
+    _need(codes, "codes", torch.int8)
+    _need(scales, "scales", torch.float16)
+    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+        raise ValueError("x must be [n_tokens, n_heads, head_dim] with contiguous (token, head) rows")
+    if codes.dim() != 3 or not codes.is_contiguous() or scales.dim() != 2 or not scales.is_contiguous():
+        raise ValueError("codes must be contiguous [n_heads, s_total, 128] and scales contiguous [n_heads, s_total]")
+    _check(lib.h3a_kv_quantize(_ptr(x), x.stride(0), x.shape[0], x.shape[1], x.shape[2], int(token_offset),
+                               codes.shape[1], _ptr(codes), _ptr(scales), _stream(x, stream)))
+
+
+def new_kvi8r_store(s_total: int, n_heads: int, device="cuda"):
+    """Allocate an empty kvi8r store: (k_codes, v_codes, scales[2, n_heads, s_total])."""
+    k = torch.empty((n_heads, s_total, HEAD_DIM), dtype=torch.int8, device=device)
+    v = torch.empty((n_heads, s_total, HEAD_DIM), dtype=torch.int8, device=device)
+    s = torch.empty((2, n_heads, s_total), dtype=torch.float16, device=device)
+    return k, v, s
+
+
+def h3a_attention_workspace_bytes(s_q: int, s_kv: int, n_heads: int, q_chunk: int, mode, sparse: bool,
+                                  head_dim: int = HEAD_DIM) -> int:
+    mode = MODES.get(mode, mode)
+    return int(_load().h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, int(mode), int(sparse)))
+
+
+def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: int = 0, mode="kvi8r",
+                  tile_mask=None, softmax_scale: float | None = None, workspace=None, stream=None):
+    """Chunked attention of q (bf16 [s_q, H, 128]) against a K/V store, written into out (bf16 [s_q, H, 128]).
+
+    mode "exact": k_store / v_store bf16 [s_kv, H, 128], scales None.
+    mode "kvi8r": k_store / v_store int8 [H, s_kv, 128], scales fp16 [2, H, s_kv].
+    tile_mask: None (dense) or uint8 [H, ceil(s_q/64), ceil(s_kv/64)].
+    workspace: a uint8 GPU tensor of at least h3a_attention_workspace_bytes; allocated here when None.
+    """
+    lib = _load()
+    mode = MODES.get(mode, mode)
+    _need(q, "q", torch.bfloat16)
+    _need(out, "out", torch.bfloat16)
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be contiguous [s_q, n_heads, head_dim] tensors of equal shape")
+    s_q, n_heads, head_dim = q.shape
+    if mode == MODE_KVI8R:
+        _need(k_store, "k_store", torch.int8)
+        _need(v_store, "v_store", torch.int8)
+        _need(scales, "scales", torch.float16)
+        s_kv = k_store.shape[1]
+    else:
+        _need(k_store, "k_store", torch.bfloat16)
+        _need(v_store, "v_store", torch.bfloat16)
+        s_kv = k_store.shape[0]
+    for name, t in (("k_store", k_store), ("v_store", v_store), ("scales", scales)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tile_mask is not None:
+        _need(tile_mask, "tile_mask", torch.uint8)
+        if not tile_mask.is_contiguous():
+            raise ValueError("tile_mask must be contiguous")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    need = int(lib.h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, int(mode),
+                                                 int(tile_mask is not None)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.h3a_attention(_ptr(q), _ptr(k_store), _ptr(v_store), _ptr(scales), s_q, s_kv, n_heads, head_dim,
+                             float(softmax_scale), int(q_chunk), int(kv_block), int(mode), _ptr(tile_mask),
+                             _ptr(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def h3a_rotate_rows(x, y, stream=None):
+    """y (fp16 [..., 128]) = x (bf16 [..., 128]) rotated into the Hadamard basis."""
+    lib = _load()
+    _need(x, "x", torch.bfloat16)
+    _need(y, "y", torch.float16)
+    if not (x.is_contiguous() and y.is_contiguous()) or x.numel() != y.numel() or x.shape[-1] != HEAD_DIM:
+        raise ValueError("x and y must be contiguous with equal sizes and rows of 128")
+    _check(lib.h3a_rotate_rows(_ptr(x), _ptr(y), x.numel() // HEAD_DIM, _stream(x, stream)))
+    return y
+
+
+def h3a_unrotate_rows(x, y, stream=None):
+    """y (bf16 [..., 128]) = x (fp32 [..., 128]) rotated back out of the Hadamard basis."""
+    lib = _load()
+    _need(x, "x", torch.float32)
+    _need(y, "y", torch.bfloat16)
+    if not (x.is_contiguous() and y.is_contiguous()) or x.numel() != y.numel() or x.shape[-1] != HEAD_DIM:
+        raise ValueError("x and y must be contiguous with equal sizes and rows of 128")
+    _check(lib.h3a_unrotate_rows(_ptr(x), _ptr(y), x.numel() // HEAD_DIM, _stream(x, stream)))
+    return y
+
+
+def h3a_timing_enable(on: bool):
+    _check(_load().h3a_timing_enable(int(bool(on))))
+
+
+def h3a_timing_collect():
+    """(summed attention-kernel milliseconds, launches) since the last collect."""
+    lib = _load()
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib.h3a_timing_collect(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,321 @@
+// C ABI entry points: argument checks, the query-chunk loop and kernel timing.
+//
+// The query-chunk loop is the one of the "H3 Streamed Blocks" node page ("How it
+// works", Inputs table q_chunk row): every chunk of q_chunk query tokens attends
+// the whole K/V store; for the kvi8r store the chunk is rotated first and its
+// output rotated back once ("Low VRAM, low RAM", "The K/V store options").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "h3a.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(H3A_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// `p` must be device-accessible memory with `bytes` bytes inside one allocation.
+int check_buffer(const void* p, uint64_t bytes, unsigned align, const char* name) {
+  if (bytes == 0) return H3A_OK;
+  if (p == nullptr) return fail(H3A_EINVAL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % align != 0) return fail(H3A_EINVAL, "%s is not %u-byte aligned", name, align);
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(H3A_EINVAL, "%s is not device memory (%s)", name, hipGetErrorString(e));
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(H3A_EINVAL, "%s is not device memory", name);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(H3A_EINVAL, "%s: cannot query its allocation (%s)", name, hipGetErrorString(e));
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+  if (q < b || (q - b) + bytes > size)
+    return fail(H3A_EINVAL, "%s: needs %llu bytes but its allocation holds %llu from this pointer", name,
+                (unsigned long long)bytes, (unsigned long long)(q >= b ? size - (q - b) : 0));
+  return H3A_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+struct WorkspaceLayout {
+  uint64_t qrot = 0, orot = 0, counts = 0, lists = 0, total = 0;
+};
+
+// Workspace per query chunk: rotated Q (fp16), rotated output (fp32), sparse kept lists.
+bool workspace_layout(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chunk, int32_t mode, bool sparse,
+                      WorkspaceLayout* w) {
+  *w = WorkspaceLayout{};
+  if (s_q <= 0 || q_chunk <= 0) return true;
+  const int64_t rows = q_chunk < s_q ? q_chunk : s_q;
+  int64_t elems;
+  if (!mul_ok(rows, (int64_t)n_heads * H3A_HEAD_DIM, &elems)) return false;
+  uint64_t off = 0;
+  if (mode == H3A_MODE_KVI8R) {
+    w->qrot = off;
+    off = align256(off + (uint64_t)elems * 2);
+    w->orot = off;
+    off = align256(off + (uint64_t)elems * 4);
+  }
+  if (sparse) {
+    const int64_t n_qt = (rows + H3A_TILE - 1) / H3A_TILE;
+    const int64_t n_kt = (s_kv + H3A_TILE - 1) / H3A_TILE;
+    int64_t nl, nc;
+    if (!mul_ok(n_qt * n_heads, n_kt, &nl) || !mul_ok(n_qt, n_heads, &nc)) return false;
+    w->counts = off;
+    off = align256(off + (uint64_t)nc * 4);
+    w->lists = off;
+    off = align256(off + (uint64_t)nl * 4);
+  }
+  w->total = off;
+  return true;
+}
+
+// ---- kernel timing --------------------------------------------------------------
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
+
+}  // namespace
+
+extern "C" {
+
+int32_t h3a_abi_version(void) { return H3A_ABI_VERSION; }
+
+const char* h3a_last_error(void) { return g_err.c_str(); }
+
+int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                        int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16, void* stream) {
+  g_err.clear();
+  if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
+  if (n_tokens < 0 || token_offset < 0 || s_total < 0)
+    return fail(H3A_EINVAL, "n_tokens, token_offset and s_total must be >= 0");
+  if (token_offset > s_total || n_tokens > s_total - token_offset)
+    return fail(H3A_EINVAL, "token_offset + n_tokens (%lld + %lld) exceeds s_total %lld", (long long)token_offset,
+                (long long)n_tokens, (long long)s_total);
+  if (x_token_stride < (int64_t)n_heads * H3A_HEAD_DIM || x_token_stride % 8 != 0)
+    return fail(H3A_EINVAL, "x_token_stride must be >= n_heads*128 and a multiple of 8 (got %lld)",
+                (long long)x_token_stride);
+  if (n_tokens == 0) return H3A_OK;
+  if (n_tokens > INT32_MAX / 2 || s_total > (int64_t)1 << 40) return fail(H3A_EINVAL, "sizes too large");
+  int64_t xb, cb, sb;
+  if (!mul_ok(n_tokens - 1, x_token_stride, &xb) || !mul_ok(s_total * n_heads, H3A_HEAD_DIM, &cb) ||
+      !mul_ok(s_total, (int64_t)n_heads * 2, &sb))
+    return fail(H3A_EINVAL, "size overflow");
+  xb = (xb + (int64_t)n_heads * H3A_HEAD_DIM) * 2;
+  int rc;
+  if ((rc = check_buffer(x, (uint64_t)xb, 16, "x")) != H3A_OK) return rc;
+  if ((rc = check_buffer(codes, (uint64_t)cb, 16, "codes")) != H3A_OK) return rc;
+  if ((rc = check_buffer(scales_f16, (uint64_t)sb, 2, "scales")) != H3A_OK) return rc;
+  hipError_t e = h3a::launch_kvi8r_quantize(static_cast<const uint16_t*>(x), x_token_stride, n_tokens, n_heads,
+                                            token_offset, s_total, codes, static_cast<uint16_t*>(scales_f16),
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3A_OK : hip_fail(e, "kvi8r_quantize launch");
+}
+
+size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, int64_t q_chunk,
+                                     int32_t mode, int32_t sparse) {
+  if (head_dim != H3A_HEAD_DIM || n_heads < 1 || s_kv < 0) return 0;
+  WorkspaceLayout w;
+  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse != 0, &w)) return 0;
+  return (size_t)w.total;
+}
+
+int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, const void* scales, int64_t s_q,
+                      int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale, int64_t q_chunk,
+                      int64_t kv_block, int32_t mode, const uint8_t* tile_mask, void* out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R) return fail(H3A_EINVAL, "unknown mode %d", mode);
+  if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
+  if (s_q < 0 || s_kv < 0) return fail(H3A_EINVAL, "s_q and s_kv must be >= 0");
+  if (s_q > ((int64_t)1 << 31) || s_kv > ((int64_t)1 << 31)) return fail(H3A_EINVAL, "sequence too long");
+  if (q_chunk < 1) return fail(H3A_EINVAL, "q_chunk must be >= 1 (got %lld)", (long long)q_chunk);
+  if (kv_block < 0 || kv_block % H3A_TILE != 0)
+    return fail(H3A_EINVAL, "kv_block must be 0 or a positive multiple of 64 (got %lld)", (long long)kv_block);
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(H3A_EINVAL, "softmax_scale must be finite and > 0");
+  const bool sparse = tile_mask != nullptr;
+  if (sparse && q_chunk % H3A_TILE != 0)
+    return fail(H3A_EINVAL, "q_chunk must be a multiple of 64 with a tile_mask (got %lld)", (long long)q_chunk);
+  if (mode == H3A_MODE_KVI8R && scales == nullptr && s_kv > 0)
+    return fail(H3A_EINVAL, "kvi8r mode needs scales");
+  if (mode == H3A_MODE_EXACT_BF16 && scales != nullptr) return fail(H3A_EINVAL, "exact mode takes no scales");
+  if (s_q == 0) return H3A_OK;
+
+  int64_t n_qkv, n_kv;
+  if (!mul_ok(s_q, (int64_t)n_heads * H3A_HEAD_DIM, &n_qkv) || !mul_ok(s_kv, (int64_t)n_heads * H3A_HEAD_DIM, &n_kv))
+    return fail(H3A_EINVAL, "size overflow");
+  const int64_t n_qt_total = (s_q + H3A_TILE - 1) / H3A_TILE, n_kt = (s_kv + H3A_TILE - 1) / H3A_TILE;
+  int rc;
+  if ((rc = check_buffer(q, (uint64_t)n_qkv * 2, 16, "q")) != H3A_OK) return rc;
+  if ((rc = check_buffer(out, (uint64_t)n_qkv * 2, 16, "out")) != H3A_OK) return rc;
+  const uint64_t kv_bytes = (uint64_t)n_kv * (mode == H3A_MODE_KVI8R ? 1 : 2);
+  if ((rc = check_buffer(k_store, kv_bytes, 16, "k_store")) != H3A_OK) return rc;
+  if ((rc = check_buffer(v_store, kv_bytes, 16, "v_store")) != H3A_OK) return rc;
+  if (mode == H3A_MODE_KVI8R && (rc = check_buffer(scales, (uint64_t)s_kv * n_heads * 4, 2, "scales")) != H3A_OK)
+    return rc;
+  if (sparse) {
+    int64_t mb;
+    if (!mul_ok(n_qt_total * n_heads, n_kt, &mb)) return fail(H3A_EINVAL, "tile_mask size overflow");
+    if ((rc = check_buffer(tile_mask, (uint64_t)mb, 1, "tile_mask")) != H3A_OK) return rc;
+  }
+  WorkspaceLayout wl;
+  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse, &wl)) return fail(H3A_EINVAL, "size overflow");
+  if (wl.total > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.total)
+      return fail(H3A_EWORKSPACE, "workspace needs %llu bytes (got %llu)", (unsigned long long)wl.total,
+                  (unsigned long long)(workspace == nullptr ? 0 : workspace_bytes));
+    if ((rc = check_buffer(workspace, wl.total, 256, "workspace")) != H3A_OK) return rc;
+  }
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  uint16_t* ob = static_cast<uint16_t*>(out);
+  bool timing;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    timing = g_timing_on;
+  }
+  for (int64_t c0 = 0; c0 < s_q; c0 += q_chunk) {
+    const int64_t rows = (s_q - c0) < q_chunk ? (s_q - c0) : q_chunk;
+    const int64_t off = c0 * n_heads * H3A_HEAD_DIM;
+    h3a::AttnChunk a{};
+    a.rows = rows;
+    a.s_kv = s_kv;
+    a.n_heads = n_heads;
+    a.scale_log2 = scale_log2;
+    a.k = k_store;
+    a.v = v_store;
+    hipError_t e;
+    if (mode == H3A_MODE_KVI8R) {
+      uint16_t* qrot = reinterpret_cast<uint16_t*>(ws + wl.qrot);
+      if ((e = h3a::launch_rotate_q(qb + off, qrot, rows * n_heads, st)) != hipSuccess)
+        return hip_fail(e, "rotate_q launch");
+      a.q = qrot;
+      a.k_scale = static_cast<const uint16_t*>(scales);
+      a.v_scale = static_cast<const uint16_t*>(scales) + s_kv * n_heads;
+      a.out = ws + wl.orot;
+    } else {
+      a.q = qb + off;
+      a.out = ob + off;
+    }
+    if (sparse) {
+      a.counts = reinterpret_cast<const int32_t*>(ws + wl.counts);
+      a.lists = reinterpret_cast<const int32_t*>(ws + wl.lists);
+      const int32_t n_qt = (int32_t)((rows + H3A_TILE - 1) / H3A_TILE);
+      if ((e = h3a::launch_route_build(tile_mask, n_qt_total, c0 / H3A_TILE, n_qt, (int32_t)n_kt, n_heads,
+                                       reinterpret_cast<int32_t*>(ws + wl.counts),
+                                       reinterpret_cast<int32_t*>(ws + wl.lists), st)) != hipSuccess)
+        return hip_fail(e, "route_build launch");
+    }
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (timing) {
+      if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess)
+        return hip_fail(e, "hipEventCreate");
+      if ((e = hipEventRecord(ev0, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if ((e = h3a::launch_attn_fwd(mode, sparse, a, st)) != hipSuccess) return hip_fail(e, "attn_fwd launch");
+    if (timing) {
+      if ((e = hipEventRecord(ev1, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      std::lock_guard<std::mutex> lk(g_timing_mu);
+      g_events.emplace_back(ev0, ev1);
+    }
+    if (mode == H3A_MODE_KVI8R) {
+      if ((e = h3a::launch_unrotate_o(reinterpret_cast<const float*>(ws + wl.orot), ob + off, rows * n_heads, st)) !=
+          hipSuccess)
+        return hip_fail(e, "unrotate_o launch");
+    }
+  }
+  return H3A_OK;
+}
+
+int32_t h3a_rotate_rows(const void* x_bf16, void* y_f16, int64_t n_rows, void* stream) {
+  g_err.clear();
+  if (n_rows < 0 || n_rows > ((int64_t)1 << 40)) return fail(H3A_EINVAL, "n_rows out of range");
+  if (n_rows == 0) return H3A_OK;
+  int rc;
+  if ((rc = check_buffer(x_bf16, (uint64_t)n_rows * 256, 16, "x")) != H3A_OK) return rc;
+  if ((rc = check_buffer(y_f16, (uint64_t)n_rows * 256, 16, "y")) != H3A_OK) return rc;
+  hipError_t e = h3a::launch_rotate_q(static_cast<const uint16_t*>(x_bf16), static_cast<uint16_t*>(y_f16), n_rows,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3A_OK : hip_fail(e, "rotate_q launch");
+}
+
+int32_t h3a_unrotate_rows(const float* x_f32, void* y_bf16, int64_t n_rows, void* stream) {
+  g_err.clear();
+  if (n_rows < 0 || n_rows > ((int64_t)1 << 40)) return fail(H3A_EINVAL, "n_rows out of range");
+  if (n_rows == 0) return H3A_OK;
+  int rc;
+  if ((rc = check_buffer(x_f32, (uint64_t)n_rows * 512, 16, "x")) != H3A_OK) return rc;
+  if ((rc = check_buffer(y_bf16, (uint64_t)n_rows * 256, 16, "y")) != H3A_OK) return rc;
+  hipError_t e = h3a::launch_unrotate_o(x_f32, static_cast<uint16_t*>(y_bf16), n_rows, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? H3A_OK : hip_fail(e, "unrotate_o launch");
+}
+
+int32_t h3a_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = on != 0;
+  return H3A_OK;
+}
+
+int32_t h3a_timing_collect(double* attn_ms, int64_t* attn_launches) {
+  g_err.clear();
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> evs;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    evs.swap(g_events);
+  }
+  double total = 0.0;
+  int rc = H3A_OK;
+  for (auto& p : evs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(p.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.first, p.second);
+    if (e != hipSuccess && rc == H3A_OK) rc = hip_fail(e, "kernel timing");
+    total += ms;
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  if (attn_ms) *attn_ms = total;
+  if (attn_launches) *attn_launches = (int64_t)evs.size();
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// kvi8r_quantize: bf16 K/V rows -> rotated int8 codes + one fp16 scale per row.
+//
+// Computes what the kv_store row of the "H3 Streamed Blocks" node page's Inputs
+// table describes for the kvi8r store (see also "Low VRAM, low RAM", "The K/V
+// store options"): rotate each (token, head) row of 128 values into the fixed
+// orthonormal Hadamard basis, take its absmax, store fp16(absmax/127) and the
+// int8 codes of the row against that stored scale.
+//
+// Layout on MI355X: one workgroup = 4 waves = 64 tokens of one head; a row is
+// handled by 4 lanes holding 32 values each, so 5 of the 7 butterfly stages
+// stay in registers and 2 use quad DPP moves.  Loads are 64 contiguous bytes
+// per lane group; codes of the 64 tokens form one contiguous 8 KB run of the
+// head-major store.  The kernel is HBM-bound: 256 B read + 130 B written per row.
+#include "h3a_device.h"
+#include "launch.h"
+
+namespace h3a {
+
+namespace {
+
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds |x| < 2^22 to an integer, ties to even
+
+__global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __restrict__ x,
+                                                             int64_t x_token_stride, int64_t n_tokens,
+                                                             int64_t token_offset, int64_t s_total,
+                                                             int8_t* __restrict__ codes,
+                                                             uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & 3;
+  const int row_in_block = (threadIdx.x >> 6) * 16 + (lane >> 2);
+  const int head = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * 64 + row_in_block;
+  const bool valid = t < n_tokens;
+
+  // Element j = 32k + 8*sub + e  <->  v[8k + e].
+  float v[32];
+  const uint16_t* src = x + (valid ? t : 0) * x_token_stride + (int64_t)head * kHeadDim;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (valid) w = *reinterpret_cast<const u32x4*>(src + 32 * k + 8 * sub);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[8 * k + 2 * i] = bf16lo_to_f32(w[i]);
+      v[8 * k + 2 * i + 1] = bf16hi_to_f32(w[i]);
+    }
+  }
+
+  fwht32_in_lane(v);
+  fwht32_cross_lane(v, sub);  // v now holds y * sqrt(128)
+
+  float a = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+  a = fmaxf(a, dpp_f32<kDppXor1>(a));
+  a = fmaxf(a, dpp_f32<kDppXor2>(a));
+
+  // scale = fp16(max|y| / 127) from the (exact) fp32 absmax, in fp64; then the
+  // reciprocal that maps unnormalised values onto the code grid.
+  const uint32_t sbits = f64_to_f16_rne_sat((double)a * kInv127Sqrt128);
+  const float r = sbits ? (float)(1.0 / (f16_bits_to_f64(sbits) * kSqrt128)) : 0.0f;
+
+  // code = clamp(round-half-even(y / s)): one fused multiply-add with the magic
+  // constant rounds the exact product once; med3 clamps to [-127, 127].
+  uint32_t packed[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float f = __builtin_fmaf(v[4 * i + j], r, kMagic);
+      f = __builtin_amdgcn_fmed3f(f, kMagic - 127.0f, kMagic + 127.0f);
+      b[j] = __float_as_uint(f);
+    }
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x0c0c0400u);
+    packed[i] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  }
+
+  if (valid) {
+    const int64_t row = (int64_t)head * s_total + token_offset + t;
+    int8_t* dst = codes + row * kHeadDim;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x2 w = {packed[2 * k], packed[2 * k + 1]};
+      *reinterpret_cast<u32x2*>(dst + 32 * k + 8 * sub) = w;
+    }
+    if (sub == 0) scales[row] = (uint16_t)sbits;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int64_t n_tokens,
+                                 int32_t n_heads, int64_t token_offset, int64_t s_total, int8_t* codes,
+                                 uint16_t* scales, hipStream_t stream) {
+  if (n_tokens == 0) return hipSuccess;
+  dim3 grid((unsigned)((n_tokens + 63) / 64), (unsigned)n_heads);
+  hipLaunchKernelGGL(kvi8r_quantize_kernel, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
+                     token_offset, s_total, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace h3a

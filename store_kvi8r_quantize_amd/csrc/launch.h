@@ -1,0 +1,43 @@
+// Internal launchers (host side); the C ABI in h3a_api.hip validates arguments
+// and then calls these.  Every launcher queues work on `stream` and returns the
+// launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h3a {
+
+hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int64_t n_tokens,
+                                 int32_t n_heads, int64_t token_offset, int64_t s_total, int8_t* codes,
+                                 uint16_t* scales, hipStream_t stream);
+
+hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
+hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
+
+// One query chunk of attention.
+struct AttnChunk {
+  const uint16_t* q;       // exact: bf16 Q rows [rows, H, 128]; kvi8r: rotated fp16 Q' [rows, H, 128]
+  const void* k;           // exact: bf16 [s_kv, H, 128]; kvi8r: int8 codes [H, s_kv, 128]
+  const void* v;
+  const uint16_t* k_scale; // kvi8r: fp16 [H, s_kv]
+  const uint16_t* v_scale;
+  void* out;               // exact: bf16 [rows, H, 128]; kvi8r: fp32 O' (normalised, rotated) [rows, H, 128]
+  const int32_t* counts;   // sparse: kept-tile count per (head, 64-row q-tile) of the chunk
+  const int32_t* lists;    // sparse: kept KV-tile indices [H, n_qtiles, n_kt], increasing
+  int64_t rows;
+  int64_t s_kv;
+  int32_t n_heads;
+  float scale_log2;        // softmax_scale * log2(e)
+};
+
+constexpr int kSparseBlockRows = 64;  // q-tile of the sparse kernel = the routing granularity
+
+hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, hipStream_t stream);
+
+// Kept-tile lists for the q-tiles [qt0, qt0 + n_qt) of every head.
+hipError_t launch_route_build(const uint8_t* mask, int64_t n_qt_total, int64_t qt0, int32_t n_qt,
+                              int32_t n_kt, int32_t n_heads, int32_t* counts, int32_t* lists,
+                              hipStream_t stream);
+
+}  // namespace h3a

@@ -80,18 +80,33 @@ def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def _round_bf16_into(buf: np.ndarray, tmp: np.ndarray, dest: np.ndarray) -> None:
+    """Same rounding as bf16_bits_from_f32, in place on reusable buffers (buf is clobbered)."""
+    u = buf.view(np.uint32)
+    np.right_shift(u, np.uint32(16), out=tmp)
+    tmp &= np.uint32(1)
+    tmp += np.uint32(0x7FFF)
+    u += tmp
+    u >>= np.uint32(16)
+    np.copyto(dest, u, casting="unsafe")
+
+
 def outlier_channels(seed: int, head: int, count: int = 4) -> np.ndarray:
     """The seeded distinct outlier channels of K for one head."""
     return np.sort(_rng(seed, STREAM_OUTLIER, head).choice(HEAD_DIM, size=count, replace=False))
 
 
-def head_rows_f32(w: Workload, tensor: str, head: int, rows: slice | None = None) -> np.ndarray:
-    """float32 [S, 128] draws for one (tensor, head) before bf16 rounding."""
+def _draw(w: Workload, tensor: str, head: int, out: np.ndarray) -> np.ndarray:
     stream = {"q": STREAM_Q, "k": STREAM_K, "v": STREAM_V}[tensor]
-    x = _rng(w.seed, stream, head).standard_normal((w.seq, HEAD_DIM), dtype=np.float32)
+    _rng(w.seed, stream, head).standard_normal(out=out, dtype=np.float32)
     if tensor == "k" and w.k_outliers:
-        x[:, outlier_channels(w.seed, head)] *= np.float32(20.0)
-    return x if rows is None else x[rows]
+        out[:, outlier_channels(w.seed, head)] *= np.float32(20.0)
+    return out
+
+
+def head_rows_f32(w: Workload, tensor: str, head: int) -> np.ndarray:
+    """float32 [S, 128] draws for one (tensor, head) before bf16 rounding."""
+    return _draw(w, tensor, head, np.empty((w.seq, HEAD_DIM), dtype=np.float32))
 
 
 def head_bf16(w: Workload, tensor: str, head: int) -> np.ndarray:
@@ -104,17 +119,39 @@ def _workers() -> int:
     return max(1, min(16, n))
 
 
+def for_each_head(w: Workload, tensors, sink, workers: int | None = None) -> None:
+    """Call sink(tensor, head, bits) for every (tensor, head), bits = uint16 [S, 128].
+
+    Draws run in a thread pool with per-thread reusable buffers; ``bits`` is
+    only valid during the call (copy it if it must outlive the call).
+    """
+    import threading
+
+    local = threading.local()
+
+    def job(th):
+        t, h = th
+        if not hasattr(local, "f"):
+            local.f = np.empty((w.seq, HEAD_DIM), dtype=np.float32)
+            local.tmp = np.empty((w.seq, HEAD_DIM), dtype=np.uint32)
+            local.bits = np.empty((w.seq, HEAD_DIM), dtype=np.uint16)
+        _draw(w, t, h, local.f)
+        _round_bf16_into(local.f, local.tmp, local.bits)
+        sink(t, h, local.bits)
+
+    jobs = [(t, h) for t in tensors for h in range(w.heads)]
+    with ThreadPoolExecutor(workers or _workers()) as ex:
+        list(ex.map(job, jobs))
+
+
 def qkv_bf16(w: Workload, tensors=("q", "k", "v")) -> dict:
     """Token-major bf16 bit patterns [S, H, 128] (uint16) for the requested tensors."""
     out = {t: np.empty((w.seq, w.heads, HEAD_DIM), dtype=np.uint16) for t in tensors}
 
-    def fill(job):
-        t, h = job
-        out[t][:, h, :] = head_bf16(w, t, h)
+    def sink(t, h, bits):
+        out[t][:, h, :] = bits
 
-    jobs = [(t, h) for t in tensors for h in range(w.heads)]
-    with ThreadPoolExecutor(_workers()) as ex:
-        list(ex.map(fill, jobs))
+    for_each_head(w, tensors, sink)
     return out
 
 

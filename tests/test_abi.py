@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every function include/h3a.h declares, and
+rejects bad arguments on the host before any GPU work (CPU only: no call here
+reaches the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import store_kvi8r_quantize_amd as h3a
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h3a.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(h3a_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(h3a.LIB_PATH):
+        pytest.fail("libh3a.so is not built (run __graft_entry__.build())")
+    return h3a.library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for need in ("h3a_kv_quantize", "h3a_attention", "h3a_attention_workspace_bytes", "h3a_abi_version",
+                 "h3a_last_error", "h3a_rotate_rows", "h3a_unrotate_rows"):
+        assert need in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version(lib):
+    assert lib.h3a_abi_version() == h3a.ABI_VERSION
+
+
+def _attn(lib, **kw):
+    a = dict(q=None, k=None, v=None, scales=None, s_q=1024, s_kv=1024, n_heads=2, head_dim=128, scale=0.088,
+             q_chunk=256, kv_block=0, mode=1, mask=None, out=None, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.h3a_attention(a["q"], a["k"], a["v"], a["scales"], a["s_q"], a["s_kv"], a["n_heads"],
+                             a["head_dim"], a["scale"], a["q_chunk"], a["kv_block"], a["mode"], a["mask"],
+                             a["out"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(head_dim=64), -2, "head_dim"),
+    (dict(mode=7), -1, "mode"),
+    (dict(n_heads=0), -1, "n_heads"),
+    (dict(s_q=-1), -1, "s_q"),
+    (dict(q_chunk=0), -1, "q_chunk"),
+    (dict(kv_block=100), -1, "kv_block"),
+    (dict(kv_block=-64), -1, "kv_block"),
+    (dict(scale=0.0), -1, "softmax_scale"),
+    (dict(scale=float("nan")), -1, "softmax_scale"),
+    (dict(mask=1, q_chunk=100), -1, "multiple of 64"),
+    (dict(mode=1, scales=None), -1, "scales"),
+    (dict(mode=0, scales=16), -1, "no scales"),
+])
+def test_attention_rejects_bad_arguments(lib, kw, status, msg):
+    assert _attn(lib, **kw) == status
+    assert msg in lib.h3a_last_error().decode()
+
+
+def test_attention_empty_query_is_noop(lib):
+    assert _attn(lib, s_q=0, scales=16) == 0
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(head_dim=96), -2, "head_dim"),
+    (dict(n_heads=0), -1, "n_heads"),
+    (dict(token_offset=1000, n_tokens=100, s_total=1024), -1, "exceeds"),
+    (dict(stride=100), -1, "x_token_stride"),
+    (dict(n_tokens=-5), -1, ">= 0"),
+])
+def test_quantize_rejects_bad_arguments(lib, kw, status, msg):
+    a = dict(x=None, stride=256, n_tokens=64, n_heads=2, head_dim=128, token_offset=0, s_total=64, codes=None,
+             scales=None, stream=None)
+    a.update(kw)
+    rc = lib.h3a_kv_quantize(a["x"], a["stride"], a["n_tokens"], a["n_heads"], a["head_dim"], a["token_offset"],
+                             a["s_total"], a["codes"], a["scales"], a["stream"])
+    assert rc == status
+    assert msg in lib.h3a_last_error().decode()
+
+
+def test_quantize_zero_tokens_is_noop(lib):
+    assert lib.h3a_kv_quantize(None, 256, 0, 2, 128, 0, 0, None, None, None) == 0
+
+
+def test_workspace_sizes(lib):
+    # kvi8r: rotated Q (fp16) + rotated output (fp32) for one chunk of rows
+    assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "kvi8r", False) == 256 * 2 * 128 * 6
+    assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "exact", False) == 0
+    assert h3a.h3a_attention_workspace_bytes(100, 1024, 2, 256, "kvi8r", False) == 100 * 2 * 128 * 6
+    # sparse adds per-(head, q-tile) counts and kept lists
+    dense = h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "exact", True)
+    assert dense >= 2 * 4 * 16 * 4 + 2 * 4 * 4
+    assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "kvi8r", False, head_dim=64) == 0

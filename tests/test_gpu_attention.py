@@ -1,0 +1,203 @@
+"""GPU parity of chunked attention (through the C ABI) against the fp64 oracle.
+
+kvi8r: relative L2 <= 2e-3 and max abs <= 1e-2 against the oracle on the GPU's
+own store (identically dequantised K/V).  Exact: relative L2 <= 4e-3 against
+the unquantised inputs, and bitwise identical across q_chunk and kv_block
+("H3 Streamed Blocks" node page, Inputs table: q_chunk "exact at any value";
+kv_block).  Tile mask: an all-ones mask reproduces dense attention bitwise,
+dropped tiles are excluded, a row with nothing kept is zero ("H3-Optimizations"
+page, Nodes).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import store_kvi8r_quantize_amd as h3a
+import synth
+from gpu_common import (EXACT_REL_L2, KVI8R_MAX_ABS, KVI8R_REL_L2, HeadSource, build_store, gpu_inputs, gpu_u16,
+                        host_u16, oracle_exact_rows, oracle_kvi8r_rows, out_rows, rel_l2, say, store_head)
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _inputs(name):
+    """(workload, host head source, GPU tensors); one workload cached at a time."""
+    if name not in _CACHE:
+        w = synth.WORKLOADS[name]
+        say("generating", name)
+        _CACHE.clear()
+        torch.cuda.empty_cache()
+        if w.seq * w.heads <= 16384 * 8:
+            bits = synth.qkv_bf16(w)
+            _CACHE[name] = (w, HeadSource(w, bits), {t: gpu_u16(bits[t]) for t in bits})
+        else:
+            _CACHE[name] = (w, HeadSource(w), gpu_inputs(w))
+    return _CACHE[name]
+
+
+def _run(mode, q, k, v, store=None, q_chunk=256, kv_block=0, mask=None):
+    out = torch.empty_like(q)
+    if mode == "kvi8r":
+        kc, vc, sc = store
+        h3a.h3a_attention(q, kc, vc, sc, out, q_chunk=q_chunk, kv_block=kv_block, mode="kvi8r", tile_mask=mask)
+    else:
+        h3a.h3a_attention(q, k, v, None, out, q_chunk=q_chunk, kv_block=kv_block, mode="exact", tile_mask=mask)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check(mode, heads, src, out, store, rows_of, mask=None, tag=""):
+    worst, mx = 0.0, 0.0
+    got_all, ref_all = [], []
+    heads = range(heads) if isinstance(heads, int) else heads
+    for h in heads:
+        rows = rows_of(h)
+        if mode == "kvi8r":
+            ref = oracle_kvi8r_rows(src, store_head(*store, h), h, rows, mask)
+        else:
+            ref = oracle_exact_rows(src, h, rows, mask)
+        got = oracle.bf16_to_f64(host_u16(out[torch.from_numpy(rows).cuda(), h]))
+        r = rel_l2(got, ref)
+        worst = max(worst, r)
+        mx = max(mx, float(np.abs(got - ref).max()))
+        got_all.append(got)
+        ref_all.append(ref)
+    total = rel_l2(np.concatenate(got_all), np.concatenate(ref_all))
+    say(tag, mode, "relL2", total, "worst head", worst, "max abs", mx)
+    if mode == "kvi8r":
+        assert total <= KVI8R_REL_L2 and mx <= KVI8R_MAX_ABS
+    else:
+        assert total <= EXACT_REL_L2
+    return total, worst, mx
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_tiny_all_rows(mode):
+    w, bits, g = _inputs("tiny")
+    store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=w.q_chunk, kv_block=w.kv_block)
+    _check(mode, w.heads, bits, out, store, lambda h: np.arange(w.seq), tag="tiny")
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_outlier16k_sampled_rows(mode):
+    w, bits, g = _inputs("outlier16k")
+    store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=w.q_chunk, kv_block=w.kv_block)
+    _check(mode, w.heads, bits, out, store, lambda h: synth.sampled_rows(w, h, 512), tag="outlier16k")
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+@pytest.mark.parametrize("s_q,s_kv,heads,q_chunk", [(1000, 777, 3, 300), (65, 1, 2, 64), (257, 129, 1, 1000)])
+def test_ragged_shapes(mode, s_q, s_kv, heads, q_chunk):
+    w = synth.Workload("ragged", max(s_q, s_kv), heads, 7, q_chunk, 0)
+    full = synth.qkv_bf16(w)
+    bits = {"q": full["q"][:s_q], "k": full["k"][:s_kv], "v": full["v"][:s_kv]}
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=q_chunk)
+    _check(mode, heads, HeadSource(w, bits), out, store, lambda h: np.arange(s_q), tag=f"ragged{s_q}x{s_kv}")
+
+
+def test_single_key_returns_value_row_exactly():
+    w = synth.Workload("one", 300, 2, 8, 128, 0)
+    bits = synth.qkv_bf16(w)
+    q, k, v = gpu_u16(bits["q"]), gpu_u16(bits["k"][:1]), gpu_u16(bits["v"][:1])
+    out = _run("exact", q, k, v, q_chunk=128)
+    assert np.array_equal(host_u16(out), np.broadcast_to(bits["v"][:1], bits["q"].shape))
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_no_keys_gives_zero(mode):
+    q = gpu_u16(synth.qkv_bf16(synth.Workload("z", 100, 2, 9, 64, 0), ("q",))["q"])
+    if mode == "kvi8r":
+        store = h3a.new_kvi8r_store(0, 2)
+        out = torch.ones_like(q)
+        h3a.h3a_attention(q, store[0], store[1], store[2], out, q_chunk=64, mode="kvi8r")
+    else:
+        e = torch.empty((0, 2, 128), dtype=torch.bfloat16, device="cuda")
+        out = torch.ones_like(q)
+        h3a.h3a_attention(q, e, e, None, out, q_chunk=64, mode="exact")
+    torch.cuda.synchronize()
+    assert not bool(out.any())
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_zero_query_averages_values(mode):
+    w, src, g = _inputs("tiny")
+    q = torch.zeros_like(g["q"])
+    store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
+    out = _run(mode, q, g["k"], g["v"], store)
+    got = oracle.bf16_to_f64(host_u16(out))
+    for h in range(w.heads):
+        if mode == "kvi8r":
+            kc, ks, vc, vs = store_head(*store, h)
+            want = oracle.dequantize_rows(vc, vs).mean(axis=0) @ oracle.orthonormal_hadamard()
+        else:
+            want = oracle.bf16_to_f64(src("v", h)).mean(axis=0)
+        assert rel_l2(got[:, h], np.broadcast_to(want, got[:, h].shape)) < 4e-3
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_q_chunk_and_kv_block_bitwise_invariance(mode):
+    w, bits, g = _inputs("outlier64k")
+    store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk) if mode == "kvi8r" else None
+    base = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=16384, kv_block=16384)
+    for q_chunk, kv_block in ((1024, 16384), (4096, 16384), (16384, 0), (4096, 4096), (1000, 64)):
+        other = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=q_chunk, kv_block=kv_block)
+        same = torch.equal(base.view(torch.int16), other.view(torch.int16))
+        say("outlier64k", mode, "q_chunk", q_chunk, "kv_block", kv_block, "bitwise equal", same)
+        assert same
+    _check(mode, range(0, w.heads, 4), bits, base, store, lambda h: synth.sampled_rows(w, h, 64),
+           tag="outlier64k")
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_all_ones_mask_equals_dense_bitwise(mode):
+    w, bits, g = _inputs("outlier16k")
+    store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
+    nt = w.n_tiles
+    ones = torch.ones((w.heads, nt, nt), dtype=torch.uint8, device="cuda")
+    dense = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=4096)
+    sparse = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=4096, mask=ones)
+    assert torch.equal(dense.view(torch.int16), sparse.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_random_mask_with_empty_tiles(mode):
+    w = synth.Workload("masked", 1000, 2, 12, 256, 0)
+    bits = synth.qkv_bf16(w)
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    nt = w.n_tiles
+    rng = np.random.default_rng(4)
+    mask = (rng.random((2, nt, nt)) < 0.3).astype(np.uint8)
+    mask[:, 3, :] = 0  # rows 192..255 keep nothing
+    store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=256, mask=torch.from_numpy(mask).cuda())
+    assert not bool(out[192:256].any())
+    _check(mode, w.heads, HeadSource(w, bits), out, store, lambda h: np.arange(w.seq), mask=mask, tag="masked")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mode", ["kvi8r", "exact"])
+def test_sparse64k_sampled_rows(mode):
+    w, bits, g = _inputs("sparse64k")
+    mask = synth.tile_mask(w)
+    store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=w.q_chunk, mask=torch.from_numpy(mask).cuda())
+
+    def rows(h):  # the dense text q-tiles' first rows plus a seeded sample of video rows
+        return np.unique(np.concatenate([np.arange(0, 512, 16), synth.sampled_rows(w, h, 64)]))
+    _check(mode, range(1, w.heads, 4), bits, out, store, rows, mask=mask, tag="sparse64k")
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("mode", ["kvi8r", "exact"])
+def test_long217k_sampled_rows(mode):
+    w, bits, g = _inputs("long217k")
+    store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=w.q_chunk, kv_block=w.kv_block)
+    _check(mode, (0, 11, 22, 31), bits, out, store, lambda h: synth.sampled_rows(w, h, 32), tag="long217k")

@@ -1,0 +1,143 @@
+"""GPU parity of kvi8r_quantize (through the C ABI) against the oracle.
+
+Codes must equal the oracle's with at most 1e-4 of them off by one (rounding
+ties), scales within 1 fp16 ulp; closed forms bit-exact; a store built in
+kv_chunk pieces equals a one-shot build bitwise ("H3 Streamed Blocks" node
+page, Inputs table, kv_chunk and kv_store rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import store_kvi8r_quantize_amd as h3a
+import synth
+from gpu_common import assert_quantize_ok, gpu_inputs, gpu_u16, host_u16, quantize_report, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _quantize(x_bits_tok_major):
+    """x: uint16 [n, H, 128] -> (codes [H, n, 128], scale bits [H, n])."""
+    n, nh, _ = x_bits_tok_major.shape
+    x = gpu_u16(x_bits_tok_major)
+    codes = torch.empty((nh, n, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((nh, n), dtype=torch.float16, device="cuda")
+    h3a.h3a_kv_quantize(x, codes, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), host_u16(scales)
+
+
+def test_closed_forms_bit_exact():
+    h = oracle.sylvester_hadamard()
+    rows = []
+    for j in (0, 1, 77, 127):
+        r = np.zeros(128, np.float32)
+        r[j] = 1.0
+        rows.append(r)
+    for i in (0, 5, 64, 127):
+        rows.append(h[i].astype(np.float32))
+    rows.append(np.zeros(128, np.float32))
+    big = np.zeros(128, np.float32)
+    big[0] = 2.0 ** 30
+    rows += [big, -big]
+    x = synth.bf16_bits_from_f32(np.stack(rows))[:, None, :]
+    codes, scales = _quantize(x)
+    codes, scales = codes[0], scales[0]
+    for n, j in enumerate((0, 1, 77, 127)):
+        assert scales[n] == 0x11B4
+        assert np.array_equal(codes[n].astype(np.int64), 127 * h[j])
+    for n, i in enumerate((0, 5, 64, 127)):
+        want = np.zeros(128, np.int8)
+        want[i] = 127
+        assert scales[4 + n] == 0x2DB4 and np.array_equal(codes[4 + n], want)
+    assert scales[8] == 0 and not codes[8].any()
+    assert scales[9] == 0x7BFF and np.all(codes[9] == 127)
+    assert scales[10] == 0x7BFF and np.all(codes[10] == -127)
+
+
+@pytest.mark.parametrize("name", ["tiny", "outlier16k"])
+@pytest.mark.parametrize("tensor", ["k", "v"])
+def test_parity_all_rows(name, tensor):
+    w = synth.WORKLOADS[name]
+    x = synth.qkv_bf16(w, (tensor,))[tensor]
+    codes, scales = _quantize(x)
+    for h in range(w.heads):
+        rep = quantize_report(x[:, h], codes[h], scales[h])
+        say(name, tensor, h, rep)
+        assert_quantize_ok(rep)
+
+
+def test_chunked_build_equals_one_shot_and_leaves_other_rows():
+    w = synth.WORKLOADS["outlier16k"]
+    x = synth.qkv_bf16(w, ("k",))["k"][:5000]
+    xg = gpu_u16(x)
+    nh = w.heads
+    one_c = torch.empty((nh, 5000, 128), dtype=torch.int8, device="cuda")
+    one_s = torch.empty((nh, 5000), dtype=torch.float16, device="cuda")
+    h3a.h3a_kv_quantize(xg, one_c, one_s)
+    # ragged chunks into a larger store pre-filled with a sentinel
+    s_total = 5200
+    cc = torch.full((nh, s_total, 128), 0x55, dtype=torch.int8, device="cuda")
+    cs = torch.full((nh, s_total), -7.0, dtype=torch.float16, device="cuda")
+    for t0 in range(0, 5000, 1000 - 23):
+        t1 = min(t0 + 977, 5000)
+        h3a.h3a_kv_quantize(xg[t0:t1], cc, cs, token_offset=100 + t0)
+    torch.cuda.synchronize()
+    assert torch.equal(cc[:, 100:5100], one_c)
+    assert np.array_equal(host_u16(cs[:, 100:5100]), host_u16(one_s))
+    assert bool((cc[:, :100] == 0x55).all()) and bool((cc[:, 5100:] == 0x55).all())
+    assert bool((cs[:, :100] == -7.0).all()) and bool((cs[:, 5100:] == -7.0).all())
+
+
+def test_strided_input_from_fused_buffer():
+    w = synth.WORKLOADS["tiny"]
+    x = synth.qkv_bf16(w, ("k",))["k"]
+    n, nh, _ = x.shape
+    fused = torch.zeros((n, 3, nh, 128), dtype=torch.bfloat16, device="cuda")
+    fused[:, 1] = gpu_u16(x)
+    codes = torch.empty((nh, n, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((nh, n), dtype=torch.float16, device="cuda")
+    h3a.h3a_kv_quantize(fused[:, 1], codes, scales)
+    c_ref, s_ref = _quantize(x)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes.cpu().numpy(), c_ref)
+    assert np.array_equal(host_u16(scales), s_ref)
+
+
+def test_rejects_buffer_too_small():
+    x = torch.zeros((128, 2, 128), dtype=torch.bfloat16, device="cuda")
+    codes = torch.empty((2, 100, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((2, 100), dtype=torch.float16, device="cuda")
+    with pytest.raises(h3a.H3AError, match="exceeds"):
+        h3a.h3a_kv_quantize(x, codes, scales)
+    # a view that claims more rows than its allocation holds is caught by the range check
+    lib = h3a.library()
+    rc = lib.h3a_kv_quantize(x.data_ptr(), 256, 128, 2, 128, 0, 100000, codes.data_ptr(), scales.data_ptr(),
+                             None)
+    assert rc == -1 and "allocation" in lib.h3a_last_error().decode()
+
+
+def test_host_pointer_rejected():
+    lib = h3a.library()
+    host = torch.zeros((64, 1, 128), dtype=torch.bfloat16)
+    codes = torch.empty((1, 64, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((1, 64), dtype=torch.float16, device="cuda")
+    rc = lib.h3a_kv_quantize(host.data_ptr(), 128, 64, 1, 128, 0, 64, codes.data_ptr(), scales.data_ptr(), None)
+    assert rc == -1 and "device memory" in lib.h3a_last_error().decode()
+
+
+@pytest.mark.timeout(600)
+def test_long217k_full_store_sampled_heads():
+    w = synth.WORKLOADS["long217k"]
+    heads = (0, 17, 31)
+    kg = gpu_inputs(w, ("k",))["k"]
+    codes = torch.empty((w.heads, w.seq, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((w.heads, w.seq), dtype=torch.float16, device="cuda")
+    for t0 in range(0, w.seq, w.q_chunk):  # kv_chunk = 16384, 13 full chunks + a 4096 tail
+        h3a.h3a_kv_quantize(kg[t0:t0 + w.q_chunk], codes, scales, token_offset=t0)
+    torch.cuda.synchronize()
+    for h in heads:
+        rep = quantize_report(synth.head_bf16(w, "k", h), codes[h].cpu().numpy(), host_u16(scales[h]))
+        say("long217k", h, rep)
+        assert_quantize_ok(rep)
