@@ -113,11 +113,12 @@ def h3a_kv_quantize(x, codes, scales, token_offset: int = 0, stream=None):
     _need(x, "x", torch.bfloat16)
     _need(codes, "codes", torch.int8)
     _need(scales, "scales", torch.float16)
-    if x.dim() != 3 or x.stride(2) != 1 or x.stride(1) != x.shape[2]:
+    if x.dim() != 3 or x.stride(2) != 1 or (x.shape[1] > 1 and x.stride(1) != x.shape[2]):
         raise ValueError("x must be [n_tokens, n_heads, head_dim] with contiguous (token, head) rows")
     if codes.dim() != 3 or not codes.is_contiguous() or scales.dim() != 2 or not scales.is_contiguous():
         raise ValueError("codes must be contiguous [n_heads, s_total, 128] and scales contiguous [n_heads, s_total]")
-    _check(lib.h3a_kv_quantize(_ptr(x), x.stride(0), x.shape[0], x.shape[1], x.shape[2], int(token_offset),
+    stride = x.stride(0) if x.shape[0] > 1 else x.shape[1] * x.shape[2]
+    _check(lib.h3a_kv_quantize(_ptr(x), stride, x.shape[0], x.shape[1], x.shape[2], int(token_offset),
                                codes.shape[1], _ptr(codes), _ptr(scales), _stream(x, stream)))
 
 

@@ -18,17 +18,25 @@
 //     lanes l and l^32).  P^T then feeds O^T += V^T P^T directly from registers
 //     as the B operand; the key order inside each 16-key step is chosen to match
 //     the accumulator layout, and V^T is read from LDS in that same order.
-//   * K/V tiles go HBM/L2 -> registers -> (kvi8r: int8 -> fp16 by byte permute
-//     into the 0x64xx exponent, one packed subtract and one packed multiply by
-//     the row scale) -> LDS, once per workgroup, double-buffered, one barrier
-//     per tile.  K is stored row-major [key][dim], V transposed [dim][key], both
-//     XOR-swizzled against bank conflicts.
-//   * Lazy rescale: the running max used for exp2 is only raised when a tile's
-//     max exceeds it by more than 2^8, so the O accumulator is rescaled a few
-//     times per row instead of every tile (P stays <= 256: safe in fp16/bf16).
+//   * K/V tiles are fetched with buffer loads whose range check zero-fills rows
+//     past the end of the store (no per-row compares), held in registers one
+//     tile ahead, and written to LDS once per workgroup: kvi8r codes become
+//     fp16 by a byte permute under the 0x64 exponent byte and one packed subtract;
+//     V rows then get one packed multiply by their scale.  K stays as exact
+//     integer codes and each key's scale (times softmax_scale * log2 e) is
+//     applied to that key's fp32 score, which keeps the fp16 rounding of
+//     code * scale out of the scores.
+//   * LDS (48.5 KB): K single-buffered [key][dim], V^T double-buffered [dim][key],
+//     both XOR-swizzled against bank conflicts; two barriers per tile.
+//   * Softmax: exponents are taken against the running max already held,
+//     p = exp2(score * c - m), in one fma.  Only when a tile's p exceeds 2^8 (the
+//     max rose by more than 8 in log2 units, and always on the first tile) does
+//     that row recompute its max, rescale O and l, and redo the tile.  Row sums
+//     add the rounded P actually fed to the matrix cores (v_dot2 with fp32
+//     accumulation).
 //   * Every per-row decision depends only on that row's scores, so a row's
 //     result is independent of q_chunk, kv_block and of which kernel variant
-//     (dense or sparse with all tiles kept) computed it.
+//     (dense, or sparse with all tiles kept) computed it.
 //   * blockIdx -> (head, q-tile) is remapped so that consecutive workgroups on
 //     one XCD (dispatch is round-robin over the 8 XCDs) share a head and
 //     reuse its K/V tiles from that XCD's L2.
@@ -39,8 +47,8 @@ namespace h3a {
 
 namespace {
 
-constexpr float kLazyThreshold = 8.0f;  // log2 units
-constexpr uint32_t kExp64 = 0x64646464u;
+constexpr float kLazyBound = 256.0f;  // 2^8: largest p allowed before the max is raised
+constexpr int kBufWord3 = 0x00020000;  // raw buffer resource, gfx9 data format word
 
 template <int MODE>
 struct Operand;
@@ -51,6 +59,10 @@ struct Operand<0> {  // exact store: bf16 operands
                                                   c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    const bf162v one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, p), one, acc, false);
+  }
 };
 template <>
 struct Operand<1> {  // kvi8r store: fp16 operands
@@ -59,69 +71,103 @@ struct Operand<1> {  // kvi8r store: fp16 operands
                                                  0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    const half2v one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, p), one, acc, false);
+  }
 };
 
-// Four int8 codes (one dword) times a row scale -> two fp16 pairs.
-__device__ __forceinline__ u32x2 dequant4(uint32_t w, half2v s2) {
-  const uint32_t u = w ^ 0x80808080u;  // code + 128 as an unsigned byte
-  const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  half2v a = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kExp64, u, 0x04010400u));  // 1024 + byte
-  half2v b = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(kExp64, u, 0x04030402u));
-  return u32x2{__builtin_bit_cast(uint32_t, (a - bias) * s2), __builtin_bit_cast(uint32_t, (b - bias) * s2)};
+// int8 codes -> fp16.  For u = code ^ 0x80 (= code + 128 as an unsigned byte),
+// the fp16 bit pattern 0x64 << 8 | u is 1024 + u; subtracting 1152 leaves the
+// code exactly.  byte_pair places bytes (0, 1) or (2, 3) of a dword under that
+// exponent.  The helpers return each pair's final bits straight from its half2
+// expression: packing fp16 pairs into a small vector, extracting and bit-casting
+// them back for more fp16 arithmetic was miscompiled (the (2, 3) pair was
+// replaced by the (0, 1) pair) by the ROCm 7.2 device compiler.
+constexpr uint32_t kSelLo = 0x04010400u, kSelHi = 0x04030402u;
+
+__device__ __forceinline__ half2v byte_pair(uint32_t u, uint32_t sel) {
+  return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, sel));
 }
 
-// Per-thread staging registers for one K/V tile.
+__device__ __forceinline__ uint32_t code_pair(uint32_t u, uint32_t sel) {
+  const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, byte_pair(u, sel) - bias);
+}
+
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t u, uint32_t sel, half2v s2) {
+  const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, (byte_pair(u, sel) - bias) * s2);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n, kBufWord3);
+}
+
+// Per-thread staging registers for one K/V tile.  K unit = one key row x 16
+// dims; V unit = 4 keys x 4 dims.
 template <int MODE, int NT>
 struct Stage {
-  static constexpr int KU = 512 / NT;  // K units (one key row x 16 dims) per thread
-  static constexpr int VU = 512 / NT;  // V units (4 keys x 4 dims) per thread
+  static constexpr int KU = 512 / NT;
+  static constexpr int VU = 512 / NT;
   u32x4 k[KU][MODE == 0 ? 2 : 1];
   uint32_t ks[KU];
   uint32_t v[VU][4][MODE == 0 ? 2 : 1];
   uint32_t vs[VU][4];
 };
 
-// Tile rows are keys kt*64 .. kt*64+63; rows >= s_kv load as zeros.
+// Tile kt of one head: rows kt*64 .. kt*64+63 of the store; rows past s_kv read
+// as 0 through the buffer range check.
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
-  const int64_t kv0 = (int64_t)kt * kTile;
+  const int64_t row0 = (int64_t)kt * kTile;
+  const int64_t left = a.s_kv - row0;  // >= 1
+  if constexpr (MODE == 0) {
+    const int rstride = a.n_heads * kHeadDim * 2;  // bytes between tokens
+    const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
+    const int64_t bytes = (left - 1) * rstride + kHeadDim * 2;
+    const auto rk = make_rsrc(static_cast<const char*>(a.k) + off0, bytes);
+    const auto rv = make_rsrc(static_cast<const char*>(a.v) + off0, bytes);
 #pragma unroll
-  for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
-    const int u = tid + NT * j;
-    const int64_t kv_raw = kv0 + (u >> 3);
-    const int d16 = u & 7;
-    const bool ok = kv_raw < a.s_kv;
-    const int64_t kv = ok ? kv_raw : 0;  // masked rows address row 0: every pointer stays in bounds
-    if constexpr (MODE == 0) {
-      const uint16_t* p = static_cast<const uint16_t*>(a.k) + (kv * a.n_heads + head) * kHeadDim + 16 * d16;
-      st.k[j][0] = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
-      st.k[j][1] = ok ? *reinterpret_cast<const u32x4*>(p + 8) : u32x4{0, 0, 0, 0};
-    } else {
-      const int64_t row = (int64_t)head * a.s_kv + kv;
-      const int8_t* p = static_cast<const int8_t*>(a.k) + row * kHeadDim + 16 * d16;
-      st.k[j][0] = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
-      st.ks[j] = ok ? a.k_scale[row] : 0u;
+    for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
+      const int u = tid + NT * j;
+      const int o = (u >> 3) * rstride + 32 * (u & 7);
+      st.k[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+      st.k[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o + 16, 0, 0));
     }
-  }
 #pragma unroll
-  for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
-    const int u = tid + NT * j;
-    const int kvg = u >> 5, dg = u & 31;
+    for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
+      const int u = tid + NT * j;
+      const int o = (4 * (u >> 5)) * rstride + 8 * (u & 31);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t kv_raw = kv0 + 4 * kvg + r;
-      const bool ok = kv_raw < a.s_kv;
-      const int64_t kv = ok ? kv_raw : 0;
-      if constexpr (MODE == 0) {
-        const uint16_t* p = static_cast<const uint16_t*>(a.v) + (kv * a.n_heads + head) * kHeadDim + 4 * dg;
-        const u32x2 w = ok ? *reinterpret_cast<const u32x2*>(p) : u32x2{0, 0};
+      for (int r = 0; r < 4; ++r) {
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, o + r * rstride, 0, 0));
         st.v[j][r][0] = w[0];
         st.v[j][r][1] = w[1];
-      } else {
-        const int64_t row = (int64_t)head * a.s_kv + kv;
-        const int8_t* p = static_cast<const int8_t*>(a.v) + row * kHeadDim + 4 * dg;
-        st.v[j][r][0] = ok ? *reinterpret_cast<const uint32_t*>(p) : 0u;
-        st.vs[j][r] = ok ? a.v_scale[row] : 0u;
+      }
+    }
+  } else {
+    const int64_t hrow = (int64_t)head * a.s_kv + row0;
+    const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, left * kHeadDim);
+    const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, left * kHeadDim);
+    const auto rks = make_rsrc(a.k_scale + hrow, left * 2);
+    const auto rvs = make_rsrc(a.v_scale + hrow, left * 2);
+#pragma unroll
+    for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
+      const int u = tid + NT * j;
+      st.k[j][0] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (u >> 3) * kHeadDim + 16 * (u & 7), 0, 0));
+      st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, (u >> 3) * 2, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
+      const int u = tid + NT * j;
+      const int r0 = 4 * (u >> 5);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        st.v[j][r][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, (r0 + r) * kHeadDim + 4 * (u & 31), 0, 0);
+        st.vs[j][r] = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + r) * 2, 0, 0);
       }
     }
   }
@@ -130,10 +176,12 @@ __device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& 
 // LDS layouts (16-bit elements):
 //   K  [64 keys][128 dims]: 16-byte chunk c of key row r lives at chunk c ^ (r & 15).
 //   V^T[128 dims][64 keys]: 8-byte unit u (4 keys) of dim row d lives at unit u ^ vswz(d).
+//   kvi8r score factors: lc[key] = key scale * softmax_scale * log2(e).
 __device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 4)) & 15; }
 
 template <int MODE, int NT>
-__device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* lk, uint16_t* lv, int tid) {
+__device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* lk, uint16_t* lv, float* lc,
+                                           float sl2, int tid) {
 #pragma unroll
   for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
     const int u = tid + NT * j;
@@ -143,12 +191,12 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
       c0 = st.k[j][0];
       c1 = st.k[j][1];
     } else {
-      const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)st.ks[j]);
-      const half2v s2 = {s, s};
-      const u32x2 e0 = dequant4(st.k[j][0][0], s2), e1 = dequant4(st.k[j][0][1], s2);
-      const u32x2 e2 = dequant4(st.k[j][0][2], s2), e3 = dequant4(st.k[j][0][3], s2);
-      c0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
-      c1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
+      const u32x4 w = st.k[j][0];
+      const uint32_t u0 = w[0] ^ 0x80808080u, u1 = w[1] ^ 0x80808080u;
+      const uint32_t u2 = w[2] ^ 0x80808080u, u3 = w[3] ^ 0x80808080u;
+      c0 = u32x4{code_pair(u0, kSelLo), code_pair(u0, kSelHi), code_pair(u1, kSelLo), code_pair(u1, kSelHi)};
+      c1 = u32x4{code_pair(u2, kSelLo), code_pair(u2, kSelHi), code_pair(u3, kSelLo), code_pair(u3, kSelHi)};
+      if (d16 == 0) lc[r] = (float)__builtin_bit_cast(_Float16, (uint16_t)st.ks[j]) * sl2;
     }
     *reinterpret_cast<u32x4*>(lk + r * kHeadDim + (((2 * d16) ^ (r & 15)) << 3)) = c0;
     *reinterpret_cast<u32x4*>(lk + r * kHeadDim + (((2 * d16 + 1) ^ (r & 15)) << 3)) = c1;
@@ -166,9 +214,9 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
       } else {
         const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)st.vs[j][r]);
         const half2v s2 = {s, s};
-        const u32x2 e = dequant4(st.v[j][r][0], s2);
-        p01[r] = e[0];
-        p23[r] = e[1];
+        const uint32_t u = st.v[j][r][0] ^ 0x80808080u;
+        p01[r] = dequant_pair(u, kSelLo, s2);
+        p23[r] = dequant_pair(u, kSelHi, s2);
       }
     }
     // transpose 4 keys x 4 dims: dim i gets (key0, key1 | key2, key3)
@@ -190,8 +238,9 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
   constexpr int NT = NW * 64;
   constexpr int BM = NW * 32;
   using Op = Operand<MODE>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTile * kHeadDim];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kTile * kHeadDim];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kHeadDim * kTile];
+  __shared__ __attribute__((aligned(16))) float lds_c[2][kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -235,14 +284,13 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
   Stage<MODE, NT> st;
   if (n_tiles > 0) {
     load_tile<MODE, NT>(st, a, head, tile_at(0), tid);
-    store_tile<MODE, NT>(st, lds_k[0], lds_v[0], tid);
+    store_tile<MODE, NT>(st, lds_k, lds_v[0], lds_c[0], sl2, tid);
   }
-  __syncthreads();
   if (n_tiles > 1) load_tile<MODE, NT>(st, a, head, tile_at(1), tid);
+  __syncthreads();
 
   for (int i = 0; i < n_tiles; ++i) {
     const int kt = tile_at(i);
-    const uint16_t* lk = lds_k[i & 1];
     const uint16_t* lv = lds_v[i & 1];
 
     // ---- S^T (64 keys x 32 queries) = K Q^T -------------------------------------
@@ -253,52 +301,83 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
       const int r = 32 * kb + c;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + r * kHeadDim + (((2 * t + g) ^ (r & 15)) << 3));
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(lds_k + r * kHeadDim + (((2 * t + g) ^ (r & 15)) << 3));
         s[kb] = Op::mfma(ka, qf[t], s[kb]);
       }
     }
+    __syncthreads();  // every wave is done reading K: the next tile may overwrite it
+    if (i + 1 < n_tiles) store_tile<MODE, NT>(st, lds_k, lds_v[(i + 1) & 1], lds_c[(i + 1) & 1], sl2, tid);
+    if (i + 2 < n_tiles) load_tile<MODE, NT>(st, a, head, tile_at(i + 2), tid);
+
+    // ---- online softmax (base 2) ----------------------------------------------
     // Accumulator register j of block kb holds key 32*kb + 8*(j/4) + 4*g + j%4.
-    if (kt >= last_full) {
+    // Exponent argument s * cf - m: cf = scale * softmax_scale * log2 e per key
+    // (kvi8r, read from LDS four keys at a time) or softmax_scale * log2 e (exact).
+    const float* lc = lds_c[i & 1];
+    auto factors = [&](int kb, int jg) -> u32x4 {
+      if constexpr (MODE == 1) return *reinterpret_cast<const u32x4*>(lc + 32 * kb + 8 * jg + 4 * g);
+      const uint32_t f = __float_as_uint(sl2);
+      return u32x4{f, f, f, f};
+    };
+    // keys of this tile that exist: 64, or fewer in the last tile
+    const int n_valid = kt >= last_full ? (int)(a.s_kv - (int64_t)kt * kTile) : kTile;
+    u32x4 pf[2][2];
+    // p = exp2(s * cf - m) for the 32 keys of this lane, packed as the B operand
+    // of the P.V product; also the max of p and the row sum of the rounded P
+    // (two chains in a fixed order) that the matrix cores will see.
+    auto exps = [&](float nm, float& pmax, float& lsum) {
+      float ls0 = 0.0f, ls1 = 0.0f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if ((int64_t)kt * kTile + 32 * kb + 8 * (j >> 2) + 4 * g + (j & 3) >= a.s_kv) s[kb][j] = -__builtin_inff();
-    }
-
-    // ---- online softmax (base 2) ----------------------------------------------
-    float mx = s[0][0];
+        for (int jg = 0; jg < 4; ++jg) {
+          const u32x4 cc = factors(kb, jg);
+          float p[4];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, s[0][j]);
+          for (int e = 0; e < 4; ++e) {
+            const float x = __builtin_fmaf(s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
+            p[e] = __builtin_amdgcn_exp2f(32 * kb + 8 * jg + 4 * g + e < n_valid ? x : -__builtin_inff());
+          }
+          pmax = fmaxf(pmax, fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])));
+          const uint32_t q01 = Op::pack(p[0], p[1]), q23 = Op::pack(p[2], p[3]);
+          if (kb == 0) {
+            ls0 = Op::sum2(q01, ls0);
+            ls0 = Op::sum2(q23, ls0);
+          } else {
+            ls1 = Op::sum2(q01, ls1);
+            ls1 = Op::sum2(q23, ls1);
+          }
+          pf[kb][jg >> 1][2 * (jg & 1)] = q01;
+          pf[kb][jg >> 1][2 * (jg & 1) + 1] = q23;
+        }
+      lsum = ls0 + ls1;
+    };
+    float pmax = 0.0f, lsum = 0.0f;
+    exps(-m_run, pmax, lsum);
+    pmax = fmaxf(pmax, xor32_f32(pmax));
+    if (!(pmax <= kLazyBound)) {
+      // This row's max rose by more than 8 (or this is its first tile): take the
+      // tile max as the new running max, rescale, and redo the exponentials.
+      float mx = -__builtin_inff();
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[1][j]);
-    mx = fmaxf(mx, xor32_f32(mx));
-    const float mt = mx * sl2;
-    if (mt > m_run + kLazyThreshold) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mt);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jg = 0; jg < 4; ++jg) {
+          const u32x4 cc = factors(kb, jg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (32 * kb + 8 * jg + 4 * g + e < n_valid) mx = fmaxf(mx, s[kb][4 * jg + e] * __uint_as_float(cc[e]));
+        }
+      mx = fmaxf(mx, xor32_f32(mx));
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
 #pragma unroll
       for (int i2 = 0; i2 < 4; ++i2) acc[i2] *= alpha;
       l_run *= alpha;
-      m_run = mt;
+      m_run = mx;
+      float unused = 0.0f;
+      exps(-m_run, unused, lsum);
     }
-    const float nm = -m_run;
-    float ls = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][j], sl2, nm));
-        s[kb][j] = p;
-        ls += p;
-      }
-    l_run += ls;
-    u32x4 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pf[kb][hf][e] = Op::pack(s[kb][8 * hf + 2 * e], s[kb][8 * hf + 2 * e + 1]);
+    l_run += lsum;
 
     // ---- O^T (128 dims x 32 queries) += V^T P^T ---------------------------------
     // k-step j covers keys 32*(j/2) + 16*(j%2) + 4g + {0..3} and the same + 8.
@@ -315,10 +394,7 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
         acc[db] = Op::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[j >> 1][j & 1], acc[db]);
       }
     }
-
-    if (i + 1 < n_tiles) store_tile<MODE, NT>(st, lds_k[(i + 1) & 1], lds_v[(i + 1) & 1], tid);
-    __syncthreads();
-    if (i + 2 < n_tiles) load_tile<MODE, NT>(st, a, head, tile_at(i + 2), tid);
+    __syncthreads();  // next tile's K / V^T / factors are in LDS; V^T[i & 1] is free again
   }
 
   // ---- epilogue: normalise and store this lane's 64 dims of its query row ------

@@ -52,9 +52,14 @@ def test_unrotate_rows(n_rows):
     h3a.h3a_unrotate_rows(torch.from_numpy(x).cuda(), y)
     got = oracle.bf16_to_f64(host_u16(y))
     ref = oracle.rotate_rows(x.astype(np.float64))  # H^T = H
-    dist = _ulp_dist(got, ref, _bf16_ulp)
-    say("unrotate", n_rows, "max ulp", dist.max())
-    assert dist.max() <= 1.0
+    # fp32 butterflies on fp32 inputs: besides the final bf16 rounding (<= 1 ulp with
+    # the fp32 error), an absolute error of a few fp32 ulps of the row's magnitude,
+    # which dominates for outputs that cancel to nearly zero.
+    fp32_abs = 8 * 2.0 ** -24 * np.abs(x).astype(np.float64).sum(axis=1, keepdims=True) / np.sqrt(128)
+    excess = np.abs(got - ref) - _bf16_ulp(np.abs(ref))
+    say("unrotate", n_rows, "max ulp", _ulp_dist(got, ref, _bf16_ulp).max(), "max excess / fp32 bound",
+        (excess / fp32_abs).max())
+    assert np.all(excess <= fp32_abs)
 
 
 def test_rotation_round_trip():
