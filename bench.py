@@ -109,6 +109,9 @@ def main() -> int:
     ap.add_argument("--workload", default="long217k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run one plain 1 GiB device-to-device copy (a known-size "
+                         "reference for HBM traffic counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -225,6 +228,13 @@ def main() -> int:
                      "launches_per_step": kern_n // args.steps, "avg_launch_ms": round(kern_avg_ms, 3),
                      "flops_per_launch": flops_per_launch},
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 1 << 30
+        del src, dst
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(w, (kc, vc, sc), args.cpu_seconds)

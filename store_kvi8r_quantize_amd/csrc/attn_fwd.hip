@@ -10,8 +10,9 @@
 // Nodes: routed 64Q x 64KV geometry, hard arm drops rejected tiles).
 //
 // MI355X design
-//   * Workgroup = NW waves x 32 query rows of one head (dense: NW = 8, 256 rows;
-//     sparse: NW = 2, one 64-row routing tile).  Key/value tiles of 64 tokens.
+//   * Workgroup = NW waves x RB blocks of 32 query rows of one head (dense: 8
+//     waves x 1 block = 256 rows, two waves per SIMD; sparse: 2 waves x 1 block,
+//     one 64-row routing tile).  Key/value tiles of 64 tokens.
 //   * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16}: the
 //     query index runs across lanes, keys across the 16 accumulator registers,
 //     so the softmax row max / row sum are in-lane (plus one exchange between
@@ -26,8 +27,8 @@
 //     integer codes and each key's scale (times softmax_scale * log2 e) is
 //     applied to that key's fp32 score, which keeps the fp16 rounding of
 //     code * scale out of the scores.
-//   * LDS (48.5 KB): K single-buffered [key][dim], V^T double-buffered [dim][key],
-//     both XOR-swizzled against bank conflicts; two barriers per tile.
+//   * LDS (64.5 KB): K [key][dim] and V^T [dim][key] double-buffered, both
+//     XOR-swizzled against bank conflicts; one barrier per tile.
 //   * Softmax: exponents are taken against the running max already held,
 //     p = exp2(score * c - m), in one fma.  Only when a tile's p exceeds 2^8 (the
 //     max rose by more than 8 in log2 units, and always on the first tile) does
@@ -40,6 +41,8 @@
 //   * blockIdx -> (head, q-tile) is remapped so that consecutive workgroups on
 //     one XCD (dispatch is round-robin over the 8 XCDs) share a head and
 //     reuse its K/V tiles from that XCD's L2.
+#include <type_traits>
+
 #include "h3a_device.h"
 #include "launch.h"
 
@@ -233,12 +236,164 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
   }
 }
 
-template <int MODE, int NW, bool SPARSE>
+// State of one 32-query block of a wave: its rows are lanes c = 0..31 (both
+// halves g = 0, 1 of the wave hold the same query, different keys / dims).
+struct RowBlock {
+  u32x4 q[8];      // B operand of S^T = K Q^T: Q[row][16t + 8g .. 16t + 8g + 7]
+  f32x16 acc[4];   // O^T accumulator: dims 32*db + 8*(j/4) + 4g + j%4, this lane's row
+  f32x16 s[2];     // S^T of the current tile: key 32*kb + 8*(j/4) + 4g + j%4
+  u32x4 pf[2][2];  // packed P of the current tile, B operand of O^T += V^T P^T
+  float m, l;      // running max (log2 units) and row sum of this lane's keys
+  int64_t row;
+  bool valid;
+};
+
+template <int MODE>
+__device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk, int c, int g) {
+  using Op = Operand<MODE>;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    rb.s[kb] = f32x16{};
+    const int r = 32 * kb + c;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + r * kHeadDim + (((2 * t + g) ^ (r & 15)) << 3));
+      rb.s[kb] = Op::mfma(ka, rb.q[t], rb.s[kb]);
+    }
+  }
+}
+
+// O^T += V^T P^T.  k-step j covers keys 32*(j/2) + 16*(j%2) + 4g + {0..3} and
+// the same + 8, matching the order of the S^T accumulator registers in pf.
+template <int MODE>
+__device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv, int c, int g) {
+  using Op = Operand<MODE>;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + c;
+    const uint16_t* row = lv + d * kTile;
+    const int sw = vswz(d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u0 = 8 * (j >> 1) + 4 * (j & 1) + g;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ((u0 ^ sw) << 2));
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + (((u0 + 2) ^ sw) << 2));
+      rb.acc[db] = Op::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, rb.pf[j >> 1][j & 1], rb.acc[db]);
+    }
+  }
+}
+
+// Score factors of this lane's keys 32*kb + 8*jg + 4g + {0..3}: key scale *
+// softmax_scale * log2 e (kvi8r, from LDS) or softmax_scale * log2 e (exact).
+template <int MODE>
+__device__ __forceinline__ u32x4 score_factors(const float* lc, float sl2, int kb, int jg, int g) {
+  if constexpr (MODE == 1) return *reinterpret_cast<const u32x4*>(lc + 32 * kb + 8 * jg + 4 * g);
+  const uint32_t f = __float_as_uint(sl2);
+  return u32x4{f, f, f, f};
+}
+
+// p = exp2(s * factor - m) for this lane's 32 keys, packed into pf; returns the
+// max of p and sets lsum to the row sum of the rounded P (two chains, fixed order).
+template <int MODE, bool PARTIAL>
+__device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float sl2, float nm, int n_valid, int g,
+                                           float& lsum) {
+  using Op = Operand<MODE>;
+  float pmax = 0.0f, ls0 = 0.0f, ls1 = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const u32x4 cc = score_factors<MODE>(lc, sl2, kb, jg, g);
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = __builtin_fmaf(rb.s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
+        if constexpr (PARTIAL) x = 32 * kb + 8 * jg + 4 * g + e < n_valid ? x : -__builtin_inff();
+        p[e] = __builtin_amdgcn_exp2f(x);
+      }
+      pmax = fmaxf(pmax, fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])));
+      const uint32_t q01 = Op::pack(p[0], p[1]), q23 = Op::pack(p[2], p[3]);
+      if (kb == 0) {
+        ls0 = Op::sum2(q01, ls0);
+        ls0 = Op::sum2(q23, ls0);
+      } else {
+        ls1 = Op::sum2(q01, ls1);
+        ls1 = Op::sum2(q23, ls1);
+      }
+      rb.pf[kb][jg >> 1][2 * (jg & 1)] = q01;
+      rb.pf[kb][jg >> 1][2 * (jg & 1) + 1] = q23;
+    }
+  lsum = ls0 + ls1;
+  return pmax;
+}
+
+// Online softmax of one tile.  Exponentials are taken against the running max
+// already held (one fma each); only when some p exceeds 2^8 (the max rose by
+// more than 8 in log2 units, and always on the first tile) does the row take
+// the tile max as its new running max, rescale O and l, and redo the tile.
+template <int MODE, bool PARTIAL>
+__device__ __forceinline__ void softmax_block(RowBlock& rb, const float* lc, float sl2, int n_valid, int g) {
+  float lsum;
+  const float pmax = pair_max(tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g, lsum));
+  if (!(pmax <= kLazyBound)) {
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const u32x4 cc = score_factors<MODE>(lc, sl2, kb, jg, g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!PARTIAL || 32 * kb + 8 * jg + 4 * g + e < n_valid)
+            mx = fmaxf(mx, rb.s[kb][4 * jg + e] * __uint_as_float(cc[e]));
+      }
+    mx = pair_max(mx);
+    const float alpha = __builtin_amdgcn_exp2f(rb.m - mx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb.acc[i] *= alpha;
+    rb.l *= alpha;
+    rb.m = mx;
+    tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g, lsum);
+  }
+  rb.l += lsum;
+}
+
+// Normalise and store this lane's 64 dims of its query row.
+template <int MODE>
+__device__ __forceinline__ void store_rows(const RowBlock& rb, const AttnChunk& a, int head, int g) {
+  const float lt = pair_sum(rb.l);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (!rb.valid) return;
+  const int64_t base = (rb.row * a.n_heads + head) * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * db + 8 * rg + 4 * g;  // accumulator registers 4rg..4rg+3 = dims d0..d0+3
+      const float o0 = rb.acc[db][4 * rg] * inv, o1 = rb.acc[db][4 * rg + 1] * inv;
+      const float o2 = rb.acc[db][4 * rg + 2] * inv, o3 = rb.acc[db][4 * rg + 3] * inv;
+      if constexpr (MODE == 0) {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + base + d0) =
+            u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      } else {
+        *reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + base + d0) =
+            u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
+      }
+    }
+}
+
+// One workgroup = NW waves x RB blocks of 32 query rows of one head.
+//   dense:  NW = 8, RB = 1 (256 rows, two waves per SIMD);
+//   sparse: NW = 2, RB = 1 (one 64-row routing tile).
+// With RB = 2 a wave would run QK_1 under softmax_0 and PV_0 under softmax_1,
+// reading each K / V^T fragment from LDS once for both blocks; the 256 VGPRs
+// a wave can use for vector work do not hold both blocks' scores, P and
+// staging at once (it spills), so the dense kernel uses RB = 1.
+template <int MODE, int NW, int RB, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
   constexpr int NT = NW * 64;
-  constexpr int BM = NW * 32;
-  using Op = Operand<MODE>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kTile * kHeadDim];
+  constexpr int BM = NW * RB * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTile * kHeadDim];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kHeadDim * kTile];
   __shared__ __attribute__((aligned(16))) float lds_c[2][kTile];
 
@@ -253,16 +408,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
   if (b < per * 8) b = (b & 7) * per + (b >> 3);
   const int head = b / n_qt;
   const int qt = b - head * n_qt;
-  const int64_t qrow = (int64_t)qt * BM + wave * 32 + c;
-  const bool qvalid = qrow < a.rows;
 
-  // B operand of S^T = K Q^T: lane holds Q[qrow][16t + 8g .. 16t + 8g + 7].
-  u32x4 qf[8];
-  {
-    const uint16_t* qp = a.q + ((qvalid ? qrow : 0) * a.n_heads + head) * kHeadDim + 8 * g;
+  RowBlock rb[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) {
+    rb[r].row = (int64_t)qt * BM + (wave * RB + r) * 32 + c;
+    rb[r].valid = rb[r].row < a.rows;
+    const uint16_t* qp = a.q + ((rb[r].valid ? rb[r].row : 0) * a.n_heads + head) * kHeadDim + 8 * g;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      qf[t] = qvalid ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+      rb[r].q[t] = rb[r].valid ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[r].acc[i] = f32x16{};
+    rb[r].m = -__builtin_inff();
+    rb[r].l = 0.0f;
   }
 
   int n_tiles = n_kt;
@@ -272,152 +431,56 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
     list = a.lists + ((int64_t)head * n_qt + qt) * n_kt;
   }
   auto tile_at = [&](int i) -> int { return SPARSE ? list[i] : i; };
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
   const float sl2 = a.scale_log2;
   const int last_full = (int)(a.s_kv / kTile);  // tiles with index >= this one are partial
 
   Stage<MODE, NT> st;
   if (n_tiles > 0) {
     load_tile<MODE, NT>(st, a, head, tile_at(0), tid);
-    store_tile<MODE, NT>(st, lds_k, lds_v[0], lds_c[0], sl2, tid);
+    store_tile<MODE, NT>(st, lds_k[0], lds_v[0], lds_c[0], sl2, tid);
   }
   if (n_tiles > 1) load_tile<MODE, NT>(st, a, head, tile_at(1), tid);
   __syncthreads();
 
-  for (int i = 0; i < n_tiles; ++i) {
-    const int kt = tile_at(i);
+  // One tile: QK_0; QK_1 + softmax_0; PV_0 + softmax_1; PV_1 + staging of the
+  // next tile.  sched_barrier(0) fences each phase: instructions interleave
+  // inside a phase but are not hoisted across it.
+  auto tile_step = [&](auto partial_tag, int i) {
+    constexpr bool kPartial = decltype(partial_tag)::value;
+    const uint16_t* lk = lds_k[i & 1];
     const uint16_t* lv = lds_v[i & 1];
-
-    // ---- S^T (64 keys x 32 queries) = K Q^T -------------------------------------
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const int r = 32 * kb + c;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const u32x4 ka = *reinterpret_cast<const u32x4*>(lds_k + r * kHeadDim + (((2 * t + g) ^ (r & 15)) << 3));
-        s[kb] = Op::mfma(ka, qf[t], s[kb]);
-      }
-    }
-    __syncthreads();  // every wave is done reading K: the next tile may overwrite it
-    if (i + 1 < n_tiles) store_tile<MODE, NT>(st, lds_k, lds_v[(i + 1) & 1], lds_c[(i + 1) & 1], sl2, tid);
-    if (i + 2 < n_tiles) load_tile<MODE, NT>(st, a, head, tile_at(i + 2), tid);
-
-    // ---- online softmax (base 2) ----------------------------------------------
-    // Accumulator register j of block kb holds key 32*kb + 8*(j/4) + 4*g + j%4.
-    // Exponent argument s * cf - m: cf = scale * softmax_scale * log2 e per key
-    // (kvi8r, read from LDS four keys at a time) or softmax_scale * log2 e (exact).
     const float* lc = lds_c[i & 1];
-    auto factors = [&](int kb, int jg) -> u32x4 {
-      if constexpr (MODE == 1) return *reinterpret_cast<const u32x4*>(lc + 32 * kb + 8 * jg + 4 * g);
-      const uint32_t f = __float_as_uint(sl2);
-      return u32x4{f, f, f, f};
-    };
-    // keys of this tile that exist: 64, or fewer in the last tile
-    const int n_valid = kt >= last_full ? (int)(a.s_kv - (int64_t)kt * kTile) : kTile;
-    u32x4 pf[2][2];
-    // p = exp2(s * cf - m) for the 32 keys of this lane, packed as the B operand
-    // of the P.V product; also the max of p and the row sum of the rounded P
-    // (two chains in a fixed order) that the matrix cores will see.
-    auto exps = [&](float nm, float& pmax, float& lsum) {
-      float ls0 = 0.0f, ls1 = 0.0f;
+    const int n_valid = kPartial ? (int)(a.s_kv - (int64_t)tile_at(i) * kTile) : kTile;
+    qk_block<MODE>(rb[0], lk, c, g);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const u32x4 cc = factors(kb, jg);
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = __builtin_fmaf(s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
-            p[e] = __builtin_amdgcn_exp2f(32 * kb + 8 * jg + 4 * g + e < n_valid ? x : -__builtin_inff());
-          }
-          pmax = fmaxf(pmax, fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])));
-          const uint32_t q01 = Op::pack(p[0], p[1]), q23 = Op::pack(p[2], p[3]);
-          if (kb == 0) {
-            ls0 = Op::sum2(q01, ls0);
-            ls0 = Op::sum2(q23, ls0);
-          } else {
-            ls1 = Op::sum2(q01, ls1);
-            ls1 = Op::sum2(q23, ls1);
-          }
-          pf[kb][jg >> 1][2 * (jg & 1)] = q01;
-          pf[kb][jg >> 1][2 * (jg & 1) + 1] = q23;
-        }
-      lsum = ls0 + ls1;
-    };
-    float pmax = 0.0f, lsum = 0.0f;
-    exps(-m_run, pmax, lsum);
-    pmax = fmaxf(pmax, xor32_f32(pmax));
-    if (!(pmax <= kLazyBound)) {
-      // This row's max rose by more than 8 (or this is its first tile): take the
-      // tile max as the new running max, rescale, and redo the exponentials.
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jg = 0; jg < 4; ++jg) {
-          const u32x4 cc = factors(kb, jg);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (32 * kb + 8 * jg + 4 * g + e < n_valid) mx = fmaxf(mx, s[kb][4 * jg + e] * __uint_as_float(cc[e]));
-        }
-      mx = fmaxf(mx, xor32_f32(mx));
-      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) acc[i2] *= alpha;
-      l_run *= alpha;
-      m_run = mx;
-      float unused = 0.0f;
-      exps(-m_run, unused, lsum);
+    for (int r = 0; r < RB; ++r) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (r + 1 < RB) qk_block<MODE>(rb[r + 1], lk, c, g);
+      if (r > 0) pv_block<MODE>(rb[r - 1], lv, c, g);
+      softmax_block<MODE, kPartial>(rb[r], lc, sl2, n_valid, g);
     }
-    l_run += lsum;
+    __builtin_amdgcn_sched_barrier(0);
+    pv_block<MODE>(rb[RB - 1], lv, c, g);
+  };
 
-    // ---- O^T (128 dims x 32 queries) += V^T P^T ---------------------------------
-    // k-step j covers keys 32*(j/2) + 16*(j%2) + 4g + {0..3} and the same + 8.
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d = 32 * db + c;
-      const uint16_t* row = lv + d * kTile;
-      const int sw = vswz(d);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int u0 = 8 * (j >> 1) + 4 * (j & 1) + g;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ((u0 ^ sw) << 2));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(row + (((u0 + 2) ^ sw) << 2));
-        acc[db] = Op::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf[j >> 1][j & 1], acc[db]);
-      }
-    }
-    __syncthreads();  // next tile's K / V^T / factors are in LDS; V^T[i & 1] is free again
+  // Only the last tile of the store can be partial (kept lists are increasing):
+  // full tiles run the loop without any key masking, a partial one runs after it.
+  const bool tail = n_tiles > 0 && tile_at(n_tiles - 1) >= last_full;
+  const int n_main = n_tiles - (tail ? 1 : 0);
+  for (int i = 0; i < n_main; ++i) {
+    tile_step(std::false_type{}, i);
+    // Stage tile i+1 into the other buffers (last read in iteration i-1, before
+    // the previous barrier), then one barrier, then fetch tile i+2.
+    if (i + 1 < n_tiles)
+      store_tile<MODE, NT>(st, lds_k[(i + 1) & 1], lds_v[(i + 1) & 1], lds_c[(i + 1) & 1], sl2, tid);
+    __syncthreads();
+    if (i + 2 < n_tiles) load_tile<MODE, NT>(st, a, head, tile_at(i + 2), tid);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (tail) tile_step(std::true_type{}, n_main);
 
-  // ---- epilogue: normalise and store this lane's 64 dims of its query row ------
-  const float lt = l_run + xor32_f32(l_run);
-  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (qvalid) {
-    const int64_t base = (qrow * a.n_heads + head) * kHeadDim;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = 32 * db + 8 * rg + 4 * g;  // accumulator registers 4rg..4rg+3 = dims d0..d0+3
-        const float o0 = acc[db][4 * rg] * inv, o1 = acc[db][4 * rg + 1] * inv;
-        const float o2 = acc[db][4 * rg + 2] * inv, o3 = acc[db][4 * rg + 3] * inv;
-        if constexpr (MODE == 0) {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + base + d0) =
-              u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-        } else {
-          *reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + base + d0) =
-              u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
-        }
-      }
-  }
+  for (int r = 0; r < RB; ++r) store_rows<MODE>(rb[r], a, head, g);
 }
 
 // Kept-tile list of one (head, q-tile) row of the mask, in increasing key order.
@@ -447,15 +510,15 @@ __global__ __launch_bounds__(256) void route_build_kernel(const uint8_t* __restr
   if (tid == 255) counts[head * n_qt + qt] = part[255];
 }
 
-template <int MODE, int NW, bool SPARSE>
+template <int MODE, int NW, int RB, bool SPARSE>
 hipError_t launch_variant(const AttnChunk& a, hipStream_t stream) {
-  constexpr int BM = NW * 32;
+  constexpr int BM = NW * RB * 32;
   const int32_t n_qt = (int32_t)((a.rows + BM - 1) / BM);
   const int32_t n_kt = (int32_t)((a.s_kv + kTile - 1) / kTile);
   const int64_t n_wg = (int64_t)n_qt * a.n_heads;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<MODE, NW, SPARSE>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a, n_qt,
-                     n_kt);
+  hipLaunchKernelGGL((attn_fwd_kernel<MODE, NW, RB, SPARSE>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a,
+                     n_qt, n_kt);
   return hipGetLastError();
 }
 
@@ -463,8 +526,9 @@ hipError_t launch_variant(const AttnChunk& a, hipStream_t stream) {
 
 hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, hipStream_t stream) {
   static_assert(kSparseBlockRows == 2 * 32, "sparse kernel covers one routing tile");
-  if (mode == 0) return sparse ? launch_variant<0, 2, true>(a, stream) : launch_variant<0, 8, false>(a, stream);
-  return sparse ? launch_variant<1, 2, true>(a, stream) : launch_variant<1, 8, false>(a, stream);
+  if (mode == 0)
+    return sparse ? launch_variant<0, 2, 1, true>(a, stream) : launch_variant<0, 8, 1, false>(a, stream);
+  return sparse ? launch_variant<1, 2, 1, true>(a, stream) : launch_variant<1, 8, 1, false>(a, stream);
 }
 
 hipError_t launch_route_build(const uint8_t* mask, int64_t n_qt_total, int64_t qt0, int32_t n_qt, int32_t n_kt,

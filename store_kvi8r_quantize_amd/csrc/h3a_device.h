@@ -67,6 +67,18 @@ __device__ __forceinline__ float xor32_f32(float x) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32) << 2), __float_as_int(x)));
 }
 
+// max / sum of x over the lane pair (l, l ^ 32), with one v_permlane32_swap:
+// after swapping the upper half of a with the lower half of b (a = b = x), lane
+// l holds x[l ^ 32] in one of the two and x[l] in the other.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- 128-point Walsh-Hadamard butterflies on 32 values held by one lane ----
 //
 // A row of 128 values is spread over 4 consecutive lanes (sub = lane & 3).
