@@ -27,8 +27,8 @@
 //     integer codes and each key's scale (times softmax_scale * log2 e) is
 //     applied to that key's fp32 score, which keeps the fp16 rounding of
 //     code * scale out of the scores.
-//   * LDS (64.5 KB): K [key][dim] and V^T [dim][key] double-buffered, both
-//     XOR-swizzled against bank conflicts; one barrier per tile.
+//   * LDS (68.5 KB): K [key][dim] and V^T [dim][key] double-buffered, rows
+//     padded against bank conflicts; one barrier per tile.
 //   * Softmax: exponents are taken against the running max already held,
 //     p = exp2(score * c - m), in one fma.  Only when a tile's p exceeds 2^8 (the
 //     max rose by more than 8 in log2 units, and always on the first tile) does
@@ -176,11 +176,18 @@ __device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& 
   }
 }
 
-// LDS layouts (16-bit elements):
-//   K  [64 keys][128 dims]: 16-byte chunk c of key row r lives at chunk c ^ (r & 15).
-//   V^T[128 dims][64 keys]: 8-byte unit u (4 keys) of dim row d lives at unit u ^ vswz(d).
+// LDS layouts (16-bit elements), rows padded so that every fragment read of a
+// wave is bank-conflict free and every lane's addresses are one base register
+// plus compile-time offsets:
+//   K  [64 keys][128 dims], row stride 136 elements (272 B): the 16 lanes of a
+//      ds_read_b128 pass hit rows r..r+15 at banks 4r mod 64, disjoint;
+//   V^T[128 dims][64 keys], row stride 68 elements (136 B): the 32 lanes of a
+//      ds_read_b64 pass hit banks 2*(17 d mod 32), disjoint.
 //   kvi8r score factors: lc[key] = key scale * softmax_scale * log2(e).
-__device__ __forceinline__ int vswz(int d) { return (d ^ (d >> 4)) & 15; }
+constexpr int kKStride = kHeadDim + 8;  // elements
+constexpr int kVStride = kTile + 4;     // elements
+constexpr int kKTileElems = kTile * kKStride;
+constexpr int kVTileElems = kHeadDim * kVStride;
 
 template <int MODE, int NT>
 __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* lk, uint16_t* lv, float* lc,
@@ -201,8 +208,8 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
       c1 = u32x4{code_pair(u2, kSelLo), code_pair(u2, kSelHi), code_pair(u3, kSelLo), code_pair(u3, kSelHi)};
       if (d16 == 0) lc[r] = (float)__builtin_bit_cast(_Float16, (uint16_t)st.ks[j]) * sl2;
     }
-    *reinterpret_cast<u32x4*>(lk + r * kHeadDim + (((2 * d16) ^ (r & 15)) << 3)) = c0;
-    *reinterpret_cast<u32x4*>(lk + r * kHeadDim + (((2 * d16 + 1) ^ (r & 15)) << 3)) = c1;
+    *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16) = c0;
+    *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
   }
 #pragma unroll
   for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
@@ -231,7 +238,7 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d = 4 * dg + i;
-      *reinterpret_cast<u32x2*>(lv + d * kTile + ((kvg ^ vswz(d)) << 2)) = t[i];
+      *reinterpret_cast<u32x2*>(lv + d * kVStride + 4 * kvg) = t[i];
     }
   }
 }
@@ -248,16 +255,16 @@ struct RowBlock {
   bool valid;
 };
 
+// lk points at this lane's K row c, dims 8g.. of the current buffer.
 template <int MODE>
-__device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk, int c, int g) {
+__device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
   using Op = Operand<MODE>;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     rb.s[kb] = f32x16{};
-    const int r = 32 * kb + c;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + r * kHeadDim + (((2 * t + g) ^ (r & 15)) << 3));
+      const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + 32 * kb * kKStride + 16 * t);
       rb.s[kb] = Op::mfma(ka, rb.q[t], rb.s[kb]);
     }
   }
@@ -265,19 +272,17 @@ __device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk, int c
 
 // O^T += V^T P^T.  k-step j covers keys 32*(j/2) + 16*(j%2) + 4g + {0..3} and
 // the same + 8, matching the order of the S^T accumulator registers in pf.
+// lv points at this lane's V^T row c, keys 4g.. of the current buffer.
 template <int MODE>
-__device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv, int c, int g) {
+__device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
   using Op = Operand<MODE>;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + c;
-    const uint16_t* row = lv + d * kTile;
-    const int sw = vswz(d);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int u0 = 8 * (j >> 1) + 4 * (j & 1) + g;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + ((u0 ^ sw) << 2));
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + (((u0 + 2) ^ sw) << 2));
+      const uint16_t* p = lv + 32 * db * kVStride + 32 * (j >> 1) + 16 * (j & 1);
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
       rb.acc[db] = Op::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, rb.pf[j >> 1][j & 1], rb.acc[db]);
     }
   }
@@ -393,8 +398,8 @@ template <int MODE, int NW, int RB, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
   constexpr int NT = NW * 64;
   constexpr int BM = NW * RB * 32;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kHeadDim * kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVTileElems];
   __shared__ __attribute__((aligned(16))) float lds_c[2][kTile];
 
   const int tid = threadIdx.x;
@@ -447,20 +452,20 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
   // inside a phase but are not hoisted across it.
   auto tile_step = [&](auto partial_tag, int i) {
     constexpr bool kPartial = decltype(partial_tag)::value;
-    const uint16_t* lk = lds_k[i & 1];
-    const uint16_t* lv = lds_v[i & 1];
+    const uint16_t* lk = lds_k[i & 1] + c * kKStride + 8 * g;
+    const uint16_t* lv = lds_v[i & 1] + c * kVStride + 4 * g;
     const float* lc = lds_c[i & 1];
     const int n_valid = kPartial ? (int)(a.s_kv - (int64_t)tile_at(i) * kTile) : kTile;
-    qk_block<MODE>(rb[0], lk, c, g);
+    qk_block<MODE>(rb[0], lk);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       __builtin_amdgcn_sched_barrier(0);
-      if (r + 1 < RB) qk_block<MODE>(rb[r + 1], lk, c, g);
-      if (r > 0) pv_block<MODE>(rb[r - 1], lv, c, g);
+      if (r + 1 < RB) qk_block<MODE>(rb[r + 1], lk);
+      if (r > 0) pv_block<MODE>(rb[r - 1], lv);
       softmax_block<MODE, kPartial>(rb[r], lc, sl2, n_valid, g);
     }
     __builtin_amdgcn_sched_barrier(0);
-    pv_block<MODE>(rb[RB - 1], lv, c, g);
+    pv_block<MODE>(rb[RB - 1], lv);
   };
 
   // Only the last tile of the store can be partial (kept lists are increasing):
@@ -481,6 +486,128 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
 
 #pragma unroll
   for (int r = 0; r < RB; ++r) store_rows<MODE>(rb[r], a, head, g);
+}
+
+// Dense kernel: 8 waves x 32 query rows = 256 rows of one head, two waves per
+// SIMD, software-pipelined across the two waves of each SIMD ("ping-pong").
+// Group 0 (waves 0-3) and group 1 (waves 4-7) hold one wave on every SIMD
+// each.  Between two barriers (one period) group 0 runs
+//     QK(i), softmax(i), PV(i), stage(i+1)
+// and group 1 runs
+//     softmax(i-1), PV(i-1), stage(i+1), QK(i)
+// so each matrix-core phase of one wave meets a vector phase of the other wave
+// on the same SIMD.  Tiles are triple-buffered in LDS: during period i tiles
+// i-1 and i are read while tile i+1 is written.  Each row's arithmetic is the
+// same as in attn_fwd_kernel, only its timing differs.
+template <int MODE>
+__global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
+  constexpr int NT = 512;
+  constexpr int BM = 256;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[3][kKTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][kVTileElems];
+  __shared__ __attribute__((aligned(16))) float lds_c[3][kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, g = lane >> 5;
+  const bool late = wave >= 4;  // group 1: runs each tile half a period behind
+
+  int b = blockIdx.x;
+  const int per = (int)gridDim.x >> 3;
+  if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  const int head = b / n_qt;
+  const int qt = b - head * n_qt;
+
+  RowBlock rb;
+  rb.row = (int64_t)qt * BM + wave * 32 + c;
+  rb.valid = rb.row < a.rows;
+  {
+    const uint16_t* qp = a.q + ((rb.valid ? rb.row : 0) * a.n_heads + head) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      rb.q[t] = rb.valid ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rb.acc[i] = f32x16{};
+  rb.m = -__builtin_inff();
+  rb.l = 0.0f;
+
+  const int n = n_kt;
+  const float sl2 = a.scale_log2;
+  const bool tail = n > 0 && (int64_t)n * kTile > a.s_kv;  // the last tile is partial
+  const int n_valid_last = n > 0 ? (int)(a.s_kv - (int64_t)(n - 1) * kTile) : 0;
+  auto lk = [&](int t) { return lds_k[t % 3] + c * kKStride + 8 * g; };
+  auto lv = [&](int t) { return lds_v[t % 3] + c * kVStride + 4 * g; };
+  auto lc = [&](int t) -> const float* { return lds_c[t % 3]; };
+  Stage<MODE, NT> st;
+  auto stage = [&](int t) {  // write tile t (held in registers) to LDS, fetch nothing
+    store_tile<MODE, NT>(st, lds_k[t % 3], lds_v[t % 3], lds_c[t % 3], sl2, tid);
+  };
+  auto sm_full = [&](int t) { softmax_block<MODE, false>(rb, lc(t), sl2, kTile, g); };
+  auto sm_last = [&](int t) {
+    if (tail)
+      softmax_block<MODE, true>(rb, lc(t), sl2, n_valid_last, g);
+    else
+      softmax_block<MODE, false>(rb, lc(t), sl2, kTile, g);
+  };
+  // end of a period: barrier, then fetch tile t into registers if it exists
+  auto end_period = [&](int t) {
+    __syncthreads();
+    if (t < n) load_tile<MODE, NT>(st, a, head, t, tid);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (n > 0) {
+    load_tile<MODE, NT>(st, a, head, 0, tid);
+    stage(0);
+  }
+  if (n > 1) load_tile<MODE, NT>(st, a, head, 1, tid);
+  __syncthreads();
+
+  if (!late) {
+    for (int i = 0; i + 1 < n; ++i) {  // periods 0 .. n-2
+      qk_block<MODE>(rb, lk(i));
+      __builtin_amdgcn_sched_barrier(0);
+      sm_full(i);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block<MODE>(rb, lv(i));
+      __builtin_amdgcn_sched_barrier(0);
+      stage(i + 1);
+      end_period(i + 2);
+    }
+    if (n > 0) {  // period n-1
+      qk_block<MODE>(rb, lk(n - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      sm_last(n - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block<MODE>(rb, lv(n - 1));
+      __syncthreads();
+    }
+    __syncthreads();  // period n: group 1 finishes tile n-1
+  } else {
+    if (n > 0) {  // period 0
+      if (n > 1) stage(1);
+      qk_block<MODE>(rb, lk(0));
+      end_period(2);
+    }
+    for (int i = 1; i < n; ++i) {  // periods 1 .. n-1
+      sm_full(i - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block<MODE>(rb, lv(i - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < n) stage(i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      qk_block<MODE>(rb, lk(i));
+      end_period(i + 2);
+    }
+    if (n > 0) {  // period n
+      sm_last(n - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block<MODE>(rb, lv(n - 1));
+    }
+    __syncthreads();
+  }
+  store_rows<MODE>(rb, a, head, g);
 }
 
 // Kept-tile list of one (head, q-tile) row of the mask, in increasing key order.
@@ -524,11 +651,20 @@ hipError_t launch_variant(const AttnChunk& a, hipStream_t stream) {
 
 }  // namespace
 
+template <int MODE>
+hipError_t launch_dense(const AttnChunk& a, hipStream_t stream) {
+  const int32_t n_qt = (int32_t)((a.rows + 255) / 256);
+  const int32_t n_kt = (int32_t)((a.s_kv + kTile - 1) / kTile);
+  const int64_t n_wg = (int64_t)n_qt * a.n_heads;
+  if (n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_dense_kernel<MODE>), dim3((unsigned)n_wg), dim3(512), 0, stream, a, n_qt, n_kt);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, hipStream_t stream) {
   static_assert(kSparseBlockRows == 2 * 32, "sparse kernel covers one routing tile");
-  if (mode == 0)
-    return sparse ? launch_variant<0, 2, 1, true>(a, stream) : launch_variant<0, 8, 1, false>(a, stream);
-  return sparse ? launch_variant<1, 2, 1, true>(a, stream) : launch_variant<1, 8, 1, false>(a, stream);
+  if (mode == 0) return sparse ? launch_variant<0, 2, 1, true>(a, stream) : launch_dense<0>(a, stream);
+  return sparse ? launch_variant<1, 2, 1, true>(a, stream) : launch_dense<1>(a, stream);
 }
 
 hipError_t launch_route_build(const uint8_t* mask, int64_t n_qt_total, int64_t qt0, int32_t n_qt, int32_t n_kt,
