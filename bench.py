@@ -66,6 +66,39 @@ def attention_flops(w, mask=None) -> float:
     return float(4.0 * 128 * np.einsum("hqk,q,k->", mask.astype(np.float64), rows, keys))
 
 
+KERNEL_SOURCES = ("store_kvi8r_quantize_amd/csrc/attn_fwd.hip", "store_kvi8r_quantize_amd/csrc/h3a_device.h",
+                  "store_kvi8r_quantize_amd/csrc/launch.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_long217k_hbm_traffic.txt")
+
+
+def measured_traffic(mode: str):
+    """HBM bytes per launch of the attention kernel from the committed FETCH_SIZE / WRITE_SIZE summary.
+
+    The summary records the sha256 of the kernel sources it was taken on; if the
+    sources have changed since, the figure no longer describes this kernel and
+    None is returned.
+    """
+    import hashlib
+
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.split()[0] if v.split() else ""
+    if vals.get("source_sha256") != h.hexdigest():
+        return None
+    v = vals.get(f"traffic_bytes_per_launch {mode}")
+    return float(v) if v else None
+
+
 def cpu_baseline(w, store, seconds: float):
     """The fp64 oracle on a bounded sample: kvi8r attention of head 0 rows against the full store."""
     import numpy as np
@@ -101,6 +134,42 @@ def cpu_baseline(w, store, seconds: float):
                       f"{w.seq} keys, in blocks of {block} rows, {el:.1f} s"}
 
 
+def sparse_leg(h3a, dev, reps: int):
+    """kvi8r attention over the 64Q x 64KV tile-masked sparse64k workload (30 % video KV density)."""
+    import torch
+
+    import synth
+
+    w = synth.WORKLOADS["sparse64k"]
+    x = make_inputs(w)
+    mask_np = synth.tile_mask(w)
+    mask = torch.from_numpy(mask_np).to(dev)
+    kc, vc, sc = h3a.new_kvi8r_store(w.seq, w.heads, device=dev)
+    for t0 in range(0, w.seq, w.q_chunk):
+        h3a.h3a_kv_quantize(x["k"][t0:t0 + w.q_chunk], kc, sc[0], token_offset=t0)
+        h3a.h3a_kv_quantize(x["v"][t0:t0 + w.q_chunk], vc, sc[1], token_offset=t0)
+    out = torch.empty_like(x["q"])
+    ws = torch.empty(max(h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, w.q_chunk, "kvi8r", True), 256),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = lambda: h3a.h3a_attention(x["q"], kc, vc, sc, out, q_chunk=w.q_chunk, mode="kvi8r", tile_mask=mask,
+                                     workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = attention_flops(w, mask_np)
+    tflops = flops / (ms / 1000) / 1e12
+    return {"workload": w.name, "mode": "kvi8r", "seq": w.seq, "heads": w.heads, "q_chunk": w.q_chunk,
+            "kept_tile_frac": round(float(mask_np.mean()), 4), "tflop_algorithmic": round(flops / 1e12, 3),
+            "ms": round(ms, 3), "tflops": round(tflops, 2), "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,6 +178,7 @@ def main() -> int:
     ap.add_argument("--workload", default="long217k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse (sparse64k) leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run one plain 1 GiB device-to-device copy (a known-size "
                          "reference for HBM traffic counters)")
@@ -222,9 +292,10 @@ def main() -> int:
         },
         "kv_quantize": {"ms": round(per["quant"], 3), "GB_per_s": round(quant_bytes / (per["quant"] / 1000) / 1e9, 1),
                         "frac_of_hbm_peak": round(quant_bytes / (per["quant"] / 1000) / 1e9 / PEAK_HBM_GBPS, 4)},
-        "roofline": {"kernel": "attn_fwd_kernel<1,8,false> (kvi8r dense)", "bound": "mfma",
+        "roofline": {"kernel": "attn_fwd_dense_kernel<1> (kvi8r, dense)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": measured_traffic("kvi8r"),
+                     "traffic_unit": "HBM bytes per launch (FETCH_SIZE x fetch factor + WRITE_SIZE x write factor)",
                      "launches_per_step": kern_n // args.steps, "avg_launch_ms": round(kern_avg_ms, 3),
                      "flops_per_launch": flops_per_launch},
     }
@@ -235,6 +306,12 @@ def main() -> int:
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 1 << 30
         del src, dst
+    if not args.no_sparse:
+        log("sparse64k leg ...")
+        del x, out_r, out_e, ws
+        torch.cuda.empty_cache()
+        res["sparse64k"] = sparse_leg(h3a, dev, reps=3)
+        log(f"sparse64k: {res['sparse64k']['tflops']} TFLOP/s")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(w, (kc, vc, sc), args.cpu_seconds)
