@@ -10,15 +10,17 @@
 // Nodes: routed 64Q x 64KV geometry, hard arm drops rejected tiles).
 //
 // MI355X design
-//   * Workgroup = NW waves x RB blocks of 32 query rows of one head (dense: 8
-//     waves x 1 block = 256 rows, two waves per SIMD; sparse: 2 waves x 1 block,
-//     one 64-row routing tile).  Key/value tiles of 64 tokens.
+//   * Dense: workgroup = 8 waves x 32 query rows = 256 rows of one head, two
+//     waves per SIMD in a ping-pong (see attn_fwd_dense_kernel).  Sparse:
+//     2 waves x 32 rows = one 64-row routing tile.  Key/value tiles of 64 tokens.
 //   * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16}: the
 //     query index runs across lanes, keys across the 16 accumulator registers,
-//     so the softmax row max / row sum are in-lane (plus one exchange between
-//     lanes l and l^32).  P^T then feeds O^T += V^T P^T directly from registers
-//     as the B operand; the key order inside each 16-key step is chosen to match
-//     the accumulator layout, and V^T is read from LDS in that same order.
+//     so the softmax row sums are in-lane (plus one exchange between lanes l
+//     and l^32).  P^T then feeds O^T += V^T P^T directly from registers as the
+//     B operand; the key order inside each 16-key step is chosen to match the
+//     accumulator layout, and V^T is read from LDS in that same order.  K and
+//     V^T fragments are read from LDS four MFMAs ahead of their use, with the
+//     independent accumulator chains interleaved.
 //   * K/V tiles are fetched with buffer loads whose range check zero-fills rows
 //     past the end of the store (no per-row compares), held in registers one
 //     tile ahead, and written to LDS once per workgroup: kvi8r codes become
@@ -27,14 +29,15 @@
 //     integer codes and each key's scale (times softmax_scale * log2 e) is
 //     applied to that key's fp32 score, which keeps the fp16 rounding of
 //     code * scale out of the scores.
-//   * LDS (68.5 KB): K [key][dim] and V^T [dim][key] double-buffered, rows
-//     padded against bank conflicts; one barrier per tile.
+//   * LDS: K [key][dim] and V^T [dim][key], rows padded so fragment reads are
+//     bank-conflict free; triple-buffered in the dense kernel (102 KB),
+//     double-buffered in the sparse one.
 //   * Softmax: exponents are taken against the running max already held,
-//     p = exp2(score * c - m), in one fma.  Only when a tile's p exceeds 2^8 (the
-//     max rose by more than 8 in log2 units, and always on the first tile) does
-//     that row recompute its max, rescale O and l, and redo the tile.  Row sums
-//     add the rounded P actually fed to the matrix cores (v_dot2 with fp32
-//     accumulation).
+//     p = exp2(score * c - m), in one fma.  Only when a row's tile sum of p
+//     exceeds 2^8 (always on the first tile) does that row recompute its max,
+//     rescale O and l, and redo the tile, so P never exceeds 2^8.  Row sums use
+//     plain and packed-fp16 adds, not v_dot2, which shares the matrix pipeline
+//     and stalls while the other wave of the SIMD issues MFMA.
 //   * Every per-row decision depends only on that row's scores, so a row's
 //     result is independent of q_chunk, kv_block and of which kernel variant
 //     (dense, or sparse with all tiles kept) computed it.
@@ -62,10 +65,6 @@ struct Operand<0> {  // exact store: bf16 operands
                                                   c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
-  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
-    const bf162v one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162v, p), one, acc, false);
-  }
 };
 template <>
 struct Operand<1> {  // kvi8r store: fp16 operands
@@ -74,10 +73,6 @@ struct Operand<1> {  // kvi8r store: fp16 operands
                                                  0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
-  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
-    const half2v one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, p), one, acc, false);
-  }
 };
 
 // int8 codes -> fp16.  For u = code ^ 0x80 (= code + 128 as an unsigned byte),
@@ -255,19 +250,31 @@ struct RowBlock {
   bool valid;
 };
 
-// lk points at this lane's K row c, dims 8g.. of the current buffer.
+// lk points at this lane's K row c, dims 8g.. of the current buffer.  The two
+// 32-key chains are interleaved and each K fragment is read from LDS four
+// MFMAs ahead of its use.
 template <int MODE>
 __device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
   using Op = Operand<MODE>;
+  constexpr int kAhead = 4;
+  u32x4 ka[16];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    rb.s[kb] = f32x16{};
+  for (int i = 0; i < 16; ++i) ka[i] = *reinterpret_cast<const u32x4*>(lk + 32 * (i & 1) * kKStride + 16 * (i >> 1));
+  f32x16 s0 = {}, s1 = {};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(lk + 32 * kb * kKStride + 16 * t);
-      rb.s[kb] = Op::mfma(ka, rb.q[t], rb.s[kb]);
-    }
+  for (int i = 0; i < 16; i += 2) {
+    s0 = Op::mfma(ka[i], rb.q[i >> 1], s0);
+    s1 = Op::mfma(ka[i + 1], rb.q[i >> 1], s1);
   }
+  rb.s[0] = s0;
+  rb.s[1] = s1;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 }
 
 // O^T += V^T P^T.  k-step j covers keys 32*(j/2) + 16*(j%2) + 4g + {0..3} and
@@ -276,16 +283,28 @@ __device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
 template <int MODE>
 __device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
   using Op = Operand<MODE>;
+  constexpr int kAhead = 4;
+  u32x4 va[16];  // k-step major, so the four accumulator chains interleave
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint16_t* p = lv + 32 * db * kVStride + 32 * (j >> 1) + 16 * (j & 1);
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
-      rb.acc[db] = Op::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, rb.pf[j >> 1][j & 1], rb.acc[db]);
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int j = i >> 2, db = i & 3;
+    const uint16_t* p = lv + 32 * db * kVStride + 32 * (j >> 1) + 16 * (j & 1);
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
+    va[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int j = i >> 2, db = i & 3;
+    rb.acc[db] = Op::mfma(va[i], rb.pf[j >> 1][j & 1], rb.acc[db]);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < 16 - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 }
 
 // Score factors of this lane's keys 32*kb + 8*jg + 4g + {0..3}: key scale *
@@ -298,12 +317,14 @@ __device__ __forceinline__ u32x4 score_factors(const float* lc, float sl2, int k
 }
 
 // p = exp2(s * factor - m) for this lane's 32 keys, packed into pf; returns the
-// max of p and sets lsum to the row sum of the rounded P (two chains, fixed order).
+// sum of this lane's p in a fixed order.  kvi8r sums the fp16-rounded P with
+// packed fp16 adds (pairs, then a tree); exact sums the fp32 p in a tree.  Row
+// sums avoid v_dot2: it runs on the matrix pipeline and stalls next to MFMA.
 template <int MODE, bool PARTIAL>
-__device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float sl2, float nm, int n_valid, int g,
-                                           float& lsum) {
+__device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float sl2, float nm, int n_valid, int g) {
   using Op = Operand<MODE>;
-  float pmax = 0.0f, ls0 = 0.0f, ls1 = 0.0f;
+  float gs[8];     // exact: sum of each group of 4
+  half2v hs[8];    // kvi8r: packed sum of each group of 4
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -316,31 +337,32 @@ __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float 
         if constexpr (PARTIAL) x = 32 * kb + 8 * jg + 4 * g + e < n_valid ? x : -__builtin_inff();
         p[e] = __builtin_amdgcn_exp2f(x);
       }
-      pmax = fmaxf(pmax, fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])));
       const uint32_t q01 = Op::pack(p[0], p[1]), q23 = Op::pack(p[2], p[3]);
-      if (kb == 0) {
-        ls0 = Op::sum2(q01, ls0);
-        ls0 = Op::sum2(q23, ls0);
-      } else {
-        ls1 = Op::sum2(q01, ls1);
-        ls1 = Op::sum2(q23, ls1);
-      }
+      if constexpr (MODE == 1)
+        hs[4 * kb + jg] = __builtin_bit_cast(half2v, q01) + __builtin_bit_cast(half2v, q23);
+      else
+        gs[4 * kb + jg] = (p[0] + p[1]) + (p[2] + p[3]);
       rb.pf[kb][jg >> 1][2 * (jg & 1)] = q01;
       rb.pf[kb][jg >> 1][2 * (jg & 1) + 1] = q23;
     }
-  lsum = ls0 + ls1;
-  return pmax;
+  if constexpr (MODE == 1) {
+    const half2v h = ((hs[0] + hs[1]) + (hs[2] + hs[3])) + ((hs[4] + hs[5]) + (hs[6] + hs[7]));
+    return (float)h[0] + (float)h[1];
+  } else {
+    return ((gs[0] + gs[1]) + (gs[2] + gs[3])) + ((gs[4] + gs[5]) + (gs[6] + gs[7]));
+  }
 }
 
 // Online softmax of one tile.  Exponentials are taken against the running max
-// already held (one fma each); only when some p exceeds 2^8 (the max rose by
-// more than 8 in log2 units, and always on the first tile) does the row take
-// the tile max as its new running max, rescale O and l, and redo the tile.
+// already held (one fma each).  Only when the row's tile sum of p exceeds 2^8
+// (so that no p can exceed 2^8 otherwise; always true on the first tile, where
+// the running max is -inf) does the row take the tile max as its new running
+// max, rescale O and l, and redo the tile.  A sum above 2^8 implies some p
+// above 2^3, so the new max is always above the old one.
 template <int MODE, bool PARTIAL>
 __device__ __forceinline__ void softmax_block(RowBlock& rb, const float* lc, float sl2, int n_valid, int g) {
-  float lsum;
-  const float pmax = pair_max(tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g, lsum));
-  if (!(pmax <= kLazyBound)) {
+  float lsum = tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g);
+  if (!(pair_max(lsum) <= kLazyBound)) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -358,7 +380,7 @@ __device__ __forceinline__ void softmax_block(RowBlock& rb, const float* lc, flo
     for (int i = 0; i < 4; ++i) rb.acc[i] *= alpha;
     rb.l *= alpha;
     rb.m = mx;
-    tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g, lsum);
+    lsum = tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g);
   }
   rb.l += lsum;
 }
@@ -499,9 +521,21 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
 // on the same SIMD.  Tiles are triple-buffered in LDS: during period i tiles
 // i-1 and i are read while tile i+1 is written.  Each row's arithmetic is the
 // same as in attn_fwd_kernel, only its timing differs.
+// Dense kernel: 8 waves x 32 query rows = 256 rows of one head, two waves per
+// SIMD, software-pipelined across the two waves of each SIMD ("ping-pong").
+// Group 0 (waves 0-3) and group 1 (waves 4-7) hold one wave on every SIMD
+// each.  Between two barriers (one period) group 0 runs
+//     QK(i), softmax(i), PV(i), stage(i+1), [barrier], fetch(i+2)
+// and group 1 runs
+//     softmax(i-1), PV(i-1), QK(i), [barrier]
+// so each matrix-core phase of one wave meets a vector phase of the other wave
+// on the same SIMD.  Group 0 alone fetches and stages the K/V tiles (it has
+// the shorter chain of dependent work), so group 1 starts its softmax right
+// after the barrier.  Tiles are triple-buffered in LDS: during period i tiles
+// i-1 and i are read while tile i+1 is written.
 template <int MODE>
 __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
-  constexpr int NT = 512;
+  constexpr int NS = 256;  // staging threads (group 0)
   constexpr int BM = 256;
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[3][kKTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[3][kVTileElems];
@@ -539,10 +573,6 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
   auto lk = [&](int t) { return lds_k[t % 3] + c * kKStride + 8 * g; };
   auto lv = [&](int t) { return lds_v[t % 3] + c * kVStride + 4 * g; };
   auto lc = [&](int t) -> const float* { return lds_c[t % 3]; };
-  Stage<MODE, NT> st;
-  auto stage = [&](int t) {  // write tile t (held in registers) to LDS, fetch nothing
-    store_tile<MODE, NT>(st, lds_k[t % 3], lds_v[t % 3], lds_c[t % 3], sl2, tid);
-  };
   auto sm_full = [&](int t) { softmax_block<MODE, false>(rb, lc(t), sl2, kTile, g); };
   auto sm_last = [&](int t) {
     if (tail)
@@ -550,21 +580,19 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
     else
       softmax_block<MODE, false>(rb, lc(t), sl2, kTile, g);
   };
-  // end of a period: barrier, then fetch tile t into registers if it exists
-  auto end_period = [&](int t) {
-    __syncthreads();
-    if (t < n) load_tile<MODE, NT>(st, a, head, t, tid);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  if (n > 0) {
-    load_tile<MODE, NT>(st, a, head, 0, tid);
-    stage(0);
-  }
-  if (n > 1) load_tile<MODE, NT>(st, a, head, 1, tid);
-  __syncthreads();
 
   if (!late) {
+    Stage<MODE, NS> st;
+    auto stage = [&](int t) {  // write tile t (held in registers) to LDS
+      store_tile<MODE, NS>(st, lds_k[t % 3], lds_v[t % 3], lds_c[t % 3], sl2, tid);
+    };
+    if (n > 0) {
+      load_tile<MODE, NS>(st, a, head, 0, tid);
+      stage(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and tile 0 are in registers on every path
+    if (n > 1) load_tile<MODE, NS>(st, a, head, 1, tid);
+    __syncthreads();
     for (int i = 0; i + 1 < n; ++i) {  // periods 0 .. n-2
       qk_block<MODE>(rb, lk(i));
       __builtin_amdgcn_sched_barrier(0);
@@ -573,7 +601,11 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
       pv_block<MODE>(rb, lv(i));
       __builtin_amdgcn_sched_barrier(0);
       stage(i + 1);
-      end_period(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      // tile i+2; past the end, reload the last tile (never staged)
+      load_tile<MODE, NS>(st, a, head, i + 2 < n ? i + 2 : n - 1, tid);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (n > 0) {  // period n-1
       qk_block<MODE>(rb, lk(n - 1));
@@ -585,20 +617,21 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
     }
     __syncthreads();  // period n: group 1 finishes tile n-1
   } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q is in registers
+    __syncthreads();
     if (n > 0) {  // period 0
-      if (n > 1) stage(1);
       qk_block<MODE>(rb, lk(0));
-      end_period(2);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
     }
     for (int i = 1; i < n; ++i) {  // periods 1 .. n-1
       sm_full(i - 1);
       __builtin_amdgcn_sched_barrier(0);
       pv_block<MODE>(rb, lv(i - 1));
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < n) stage(i + 1);
-      __builtin_amdgcn_sched_barrier(0);
       qk_block<MODE>(rb, lk(i));
-      end_period(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
     }
     if (n > 0) {  // period n
       sm_last(n - 1);
