@@ -112,21 +112,19 @@ struct Stage {
   u32x4 k[KU][MODE == 0 ? 2 : 1];
   uint32_t ks[KU];
   uint32_t v[VU][4][MODE == 0 ? 2 : 1];
-  uint32_t vs[VU][4];
+  uint32_t vs[VU][2];  // kvi8r: fp16 scales of the unit's 4 keys, packed in pairs
 };
 
 // Tile kt of one head: rows kt*64 .. kt*64+63 of the store; rows past s_kv read
-// as 0 through the buffer range check.
+// as 0 through the buffer range check.  K and V parts can be fetched separately.
 template <int MODE, int NT>
-__device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
+__device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
   const int64_t row0 = (int64_t)kt * kTile;
   const int64_t left = a.s_kv - row0;  // >= 1
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;  // bytes between tokens
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
-    const int64_t bytes = (left - 1) * rstride + kHeadDim * 2;
-    const auto rk = make_rsrc(static_cast<const char*>(a.k) + off0, bytes);
-    const auto rv = make_rsrc(static_cast<const char*>(a.v) + off0, bytes);
+    const auto rk = make_rsrc(static_cast<const char*>(a.k) + off0, (left - 1) * rstride + kHeadDim * 2);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
       const int u = tid + NT * j;
@@ -134,6 +132,28 @@ __device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& 
       st.k[j][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
       st.k[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o + 16, 0, 0));
     }
+  } else {
+    const int64_t hrow = (int64_t)head * a.s_kv + row0;
+    const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, left * kHeadDim);
+    const auto rks = make_rsrc(a.k_scale + hrow, left * 2);
+#pragma unroll
+    for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
+      const int u = tid + NT * j;
+      st.k[j][0] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (u >> 3) * kHeadDim + 16 * (u & 7), 0, 0));
+      st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, (u >> 3) * 2, 0, 0);
+    }
+  }
+}
+
+template <int MODE, int NT>
+__device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
+  const int64_t row0 = (int64_t)kt * kTile;
+  const int64_t left = a.s_kv - row0;  // >= 1
+  if constexpr (MODE == 0) {
+    const int rstride = a.n_heads * kHeadDim * 2;
+    const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
+    const auto rv = make_rsrc(static_cast<const char*>(a.v) + off0, (left - 1) * rstride + kHeadDim * 2);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
@@ -147,28 +167,35 @@ __device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& 
     }
   } else {
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
-    const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, left * kHeadDim);
     const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, left * kHeadDim);
-    const auto rks = make_rsrc(a.k_scale + hrow, left * 2);
     const auto rvs = make_rsrc(a.v_scale + hrow, left * 2);
-#pragma unroll
-    for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
-      const int u = tid + NT * j;
-      st.k[j][0] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (u >> 3) * kHeadDim + 16 * (u & 7), 0, 0));
-      st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, (u >> 3) * 2, 0, 0);
-    }
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
       const int r0 = 4 * (u >> 5);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < 4; ++r)
         st.v[j][r][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, (r0 + r) * kHeadDim + 4 * (u & 31), 0, 0);
-        st.vs[j][r] = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + r) * 2, 0, 0);
+      if (left >= kTile && (hrow & 3) == 0) {  // whole tile in range, 8-byte aligned: the 4 scales in one load
+        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, r0 * 2, 0, 0));
+        st.vs[j][0] = w[0];
+        st.vs[j][1] = w[1];
+      } else {  // partial tile or unaligned: each scale on its own, rows past the end read as 0
+        const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b16(rvs, r0 * 2, 0, 0);
+        const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + 1) * 2, 0, 0);
+        const uint32_t s2 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + 2) * 2, 0, 0);
+        const uint32_t s3 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + 3) * 2, 0, 0);
+        st.vs[j][0] = (s0 & 0xFFFFu) | (s1 << 16);
+        st.vs[j][1] = (s2 & 0xFFFFu) | (s3 << 16);
       }
     }
   }
+}
+
+template <int MODE, int NT>
+__device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
+  load_tile_k<MODE, NT>(st, a, head, kt, tid);
+  load_tile_v<MODE, NT>(st, a, head, kt, tid);
 }
 
 // LDS layouts (16-bit elements), rows padded so that every fragment read of a
@@ -185,8 +212,7 @@ constexpr int kKTileElems = kTile * kKStride;
 constexpr int kVTileElems = kHeadDim * kVStride;
 
 template <int MODE, int NT>
-__device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* lk, uint16_t* lv, float* lc,
-                                           float sl2, int tid) {
+__device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t* lk, float* lc, float sl2, int tid) {
 #pragma unroll
   for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
     const int u = tid + NT * j;
@@ -206,6 +232,10 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16) = c0;
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
   }
+}
+
+template <int MODE, int NT>
+__device__ __forceinline__ void store_tile_v(const Stage<MODE, NT>& st, uint16_t* lv, int tid) {
 #pragma unroll
   for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
     const int u = tid + NT * j;
@@ -217,11 +247,12 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
         p01[r] = st.v[j][r][0];
         p23[r] = st.v[j][r][1];
       } else {
-        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)st.vs[j][r]);
+        const uint32_t sw = st.vs[j][r >> 1];
+        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? sw >> 16 : sw & 0xFFFFu));
         const half2v s2 = {s, s};
-        const uint32_t u = st.v[j][r][0] ^ 0x80808080u;
-        p01[r] = dequant_pair(u, kSelLo, s2);
-        p23[r] = dequant_pair(u, kSelHi, s2);
+        const uint32_t w = st.v[j][r][0] ^ 0x80808080u;
+        p01[r] = dequant_pair(w, kSelLo, s2);
+        p23[r] = dequant_pair(w, kSelHi, s2);
       }
     }
     // transpose 4 keys x 4 dims: dim i gets (key0, key1 | key2, key3)
@@ -236,6 +267,13 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
       *reinterpret_cast<u32x2*>(lv + d * kVStride + 4 * kvg) = t[i];
     }
   }
+}
+
+template <int MODE, int NT>
+__device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* lk, uint16_t* lv, float* lc,
+                                           float sl2, int tid) {
+  store_tile_k<MODE, NT>(st, lk, lc, sl2, tid);
+  store_tile_v<MODE, NT>(st, lv, tid);
 }
 
 // State of one 32-query block of a wave: its rows are lanes c = 0..31 (both
@@ -409,20 +447,21 @@ __device__ __forceinline__ void store_rows(const RowBlock& rb, const AttnChunk& 
     }
 }
 
-// One workgroup = NW waves x RB blocks of 32 query rows of one head.
-//   dense:  NW = 8, RB = 1 (256 rows, two waves per SIMD);
-//   sparse: NW = 2, RB = 1 (one 64-row routing tile).
-// With RB = 2 a wave would run QK_1 under softmax_0 and PV_0 under softmax_1,
-// reading each K / V^T fragment from LDS once for both blocks; the 256 VGPRs
-// a wave can use for vector work do not hold both blocks' scores, P and
-// staging at once (it spills), so the dense kernel uses RB = 1.
-template <int MODE, int NW, int RB, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
-  constexpr int NT = NW * 64;
-  constexpr int BM = NW * RB * 32;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVTileElems];
-  __shared__ __attribute__((aligned(16))) float lds_c[2][kTile];
+// Block-sparse kernel: one workgroup = 2 waves x 32 rows = one 64-row routing
+// q-tile of one head, iterating only the KV tiles its mask row keeps, in
+// increasing order.  A single LDS buffer (35 KB) and at most 256 registers per
+// wave let four workgroups share a CU, two waves per SIMD, so one workgroup's
+// staging and softmax run under another's matrix-core work.  Per kept tile:
+//     stage(i) [barrier] fetch(i+1), QK(i), softmax(i), PV(i) [barrier]
+// Each row's arithmetic is that of the dense kernel.
+template <int MODE>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_sparse_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
+  constexpr int NT = 128;
+  constexpr int BM = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kKTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kVTileElems];
+  __shared__ __attribute__((aligned(16))) float lds_c[kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -436,91 +475,63 @@ __global__ __launch_bounds__(NW * 64) void attn_fwd_kernel(AttnChunk a, int32_t 
   const int head = b / n_qt;
   const int qt = b - head * n_qt;
 
-  RowBlock rb[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    rb[r].row = (int64_t)qt * BM + (wave * RB + r) * 32 + c;
-    rb[r].valid = rb[r].row < a.rows;
-    const uint16_t* qp = a.q + ((rb[r].valid ? rb[r].row : 0) * a.n_heads + head) * kHeadDim + 8 * g;
+  RowBlock rb;
+  rb.row = (int64_t)qt * BM + wave * 32 + c;
+  rb.valid = rb.row < a.rows;
+  {
+    const uint16_t* qp = a.q + ((rb.valid ? rb.row : 0) * a.n_heads + head) * kHeadDim + 8 * g;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      rb[r].q[t] = rb[r].valid ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+      rb.q[t] = rb.valid ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rb[r].acc[i] = f32x16{};
-    rb[r].m = -__builtin_inff();
-    rb[r].l = 0.0f;
-  }
+  for (int i = 0; i < 4; ++i) rb.acc[i] = f32x16{};
+  rb.m = -__builtin_inff();
+  rb.l = 0.0f;
 
-  int n_tiles = n_kt;
-  const int32_t* list = nullptr;
-  if (SPARSE) {
-    n_tiles = a.counts[head * n_qt + qt];
-    list = a.lists + ((int64_t)head * n_qt + qt) * n_kt;
-  }
-  auto tile_at = [&](int i) -> int { return SPARSE ? list[i] : i; };
+  const int n_tiles = a.counts[head * n_qt + qt];
+  const int32_t* list = a.lists + ((int64_t)head * n_qt + qt) * n_kt;
   const float sl2 = a.scale_log2;
   const int last_full = (int)(a.s_kv / kTile);  // tiles with index >= this one are partial
+  const uint16_t* lk = lds_k + c * kKStride + 8 * g;
+  const uint16_t* lv = lds_v + c * kVStride + 4 * g;
 
   Stage<MODE, NT> st;
-  if (n_tiles > 0) {
-    load_tile<MODE, NT>(st, a, head, tile_at(0), tid);
-    store_tile<MODE, NT>(st, lds_k[0], lds_v[0], lds_c[0], sl2, tid);
-  }
-  if (n_tiles > 1) load_tile<MODE, NT>(st, a, head, tile_at(1), tid);
-  __syncthreads();
+  if (n_tiles > 0) load_tile<MODE, NT>(st, a, head, list[0], tid);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile are in registers on every path
 
-  // One tile: QK_0; QK_1 + softmax_0; PV_0 + softmax_1; PV_1 + staging of the
-  // next tile.  sched_barrier(0) fences each phase: instructions interleave
-  // inside a phase but are not hoisted across it.
-  auto tile_step = [&](auto partial_tag, int i) {
-    constexpr bool kPartial = decltype(partial_tag)::value;
-    const uint16_t* lk = lds_k[i & 1] + c * kKStride + 8 * g;
-    const uint16_t* lv = lds_v[i & 1] + c * kVStride + 4 * g;
-    const float* lc = lds_c[i & 1];
-    const int n_valid = kPartial ? (int)(a.s_kv - (int64_t)tile_at(i) * kTile) : kTile;
-    qk_block<MODE>(rb[0], lk);
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (r + 1 < RB) qk_block<MODE>(rb[r + 1], lk);
-      if (r > 0) pv_block<MODE>(rb[r - 1], lv);
-      softmax_block<MODE, kPartial>(rb[r], lc, sl2, n_valid, g);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    pv_block<MODE>(rb[RB - 1], lv);
-  };
-
-  // Only the last tile of the store can be partial (kept lists are increasing):
-  // full tiles run the loop without any key masking, a partial one runs after it.
-  const bool tail = n_tiles > 0 && tile_at(n_tiles - 1) >= last_full;
+  // Only the last kept tile can be partial (lists are increasing): full tiles
+  // run the loop without key masking, a partial one runs after it.
+  const bool tail = n_tiles > 0 && list[n_tiles - 1] >= last_full;
   const int n_main = n_tiles - (tail ? 1 : 0);
   for (int i = 0; i < n_main; ++i) {
-    tile_step(std::false_type{}, i);
-    // Stage tile i+1 into the other buffers (last read in iteration i-1, before
-    // the previous barrier), then one barrier, then fetch tile i+2.
-    if (i + 1 < n_tiles)
-      store_tile<MODE, NT>(st, lds_k[(i + 1) & 1], lds_v[(i + 1) & 1], lds_c[(i + 1) & 1], sl2, tid);
-    __syncthreads();
-    if (i + 2 < n_tiles) load_tile<MODE, NT>(st, a, head, tile_at(i + 2), tid);
+    store_tile<MODE, NT>(st, lds_k, lds_v, lds_c, sl2, tid);
     __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    const int nxt = list[i + 1 < n_tiles ? i + 1 : i];  // past the end: reload this tile, never staged
+    load_tile_v<MODE, NT>(st, a, head, nxt, tid);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_block<MODE>(rb, lk);
+    __builtin_amdgcn_sched_barrier(0);
+    softmax_block<MODE, false>(rb, lds_c, sl2, kTile, g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile_k<MODE, NT>(st, a, head, nxt, tid);  // K registers stay free through QK and softmax
+    __builtin_amdgcn_sched_barrier(0);
+    pv_block<MODE>(rb, lv);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
   }
-  if (tail) tile_step(std::true_type{}, n_main);
-
-#pragma unroll
-  for (int r = 0; r < RB; ++r) store_rows<MODE>(rb[r], a, head, g);
+  if (tail) {
+    store_tile<MODE, NT>(st, lds_k, lds_v, lds_c, sl2, tid);
+    __syncthreads();
+    const int n_valid = (int)(a.s_kv - (int64_t)list[n_main] * kTile);
+    qk_block<MODE>(rb, lk);
+    softmax_block<MODE, true>(rb, lds_c, sl2, n_valid, g);
+    pv_block<MODE>(rb, lv);
+  }
+  store_rows<MODE>(rb, a, head, g);
 }
 
-// Dense kernel: 8 waves x 32 query rows = 256 rows of one head, two waves per
-// SIMD, software-pipelined across the two waves of each SIMD ("ping-pong").
-// Group 0 (waves 0-3) and group 1 (waves 4-7) hold one wave on every SIMD
-// each.  Between two barriers (one period) group 0 runs
-//     QK(i), softmax(i), PV(i), stage(i+1)
-// and group 1 runs
-//     softmax(i-1), PV(i-1), stage(i+1), QK(i)
-// so each matrix-core phase of one wave meets a vector phase of the other wave
-// on the same SIMD.  Tiles are triple-buffered in LDS: during period i tiles
-// i-1 and i are read while tile i+1 is written.  Each row's arithmetic is the
-// same as in attn_fwd_kernel, only its timing differs.
 // Dense kernel: 8 waves x 32 query rows = 256 rows of one head, two waves per
 // SIMD, software-pipelined across the two waves of each SIMD ("ping-pong").
 // Group 0 (waves 0-3) and group 1 (waves 4-7) hold one wave on every SIMD
@@ -670,15 +681,13 @@ __global__ __launch_bounds__(256) void route_build_kernel(const uint8_t* __restr
   if (tid == 255) counts[head * n_qt + qt] = part[255];
 }
 
-template <int MODE, int NW, int RB, bool SPARSE>
-hipError_t launch_variant(const AttnChunk& a, hipStream_t stream) {
-  constexpr int BM = NW * RB * 32;
-  const int32_t n_qt = (int32_t)((a.rows + BM - 1) / BM);
+template <int MODE>
+hipError_t launch_sparse(const AttnChunk& a, hipStream_t stream) {
+  const int32_t n_qt = (int32_t)((a.rows + kSparseBlockRows - 1) / kSparseBlockRows);
   const int32_t n_kt = (int32_t)((a.s_kv + kTile - 1) / kTile);
   const int64_t n_wg = (int64_t)n_qt * a.n_heads;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_kernel<MODE, NW, RB, SPARSE>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, a,
-                     n_qt, n_kt);
+  hipLaunchKernelGGL((attn_fwd_sparse_kernel<MODE>), dim3((unsigned)n_wg), dim3(128), 0, stream, a, n_qt, n_kt);
   return hipGetLastError();
 }
 
@@ -696,8 +705,8 @@ hipError_t launch_dense(const AttnChunk& a, hipStream_t stream) {
 
 hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, hipStream_t stream) {
   static_assert(kSparseBlockRows == 2 * 32, "sparse kernel covers one routing tile");
-  if (mode == 0) return sparse ? launch_variant<0, 2, 1, true>(a, stream) : launch_dense<0>(a, stream);
-  return sparse ? launch_variant<1, 2, 1, true>(a, stream) : launch_dense<1>(a, stream);
+  if (mode == 0) return sparse ? launch_sparse<0>(a, stream) : launch_dense<0>(a, stream);
+  return sparse ? launch_sparse<1>(a, stream) : launch_dense<1>(a, stream);
 }
 
 hipError_t launch_route_build(const uint8_t* mask, int64_t n_qt_total, int64_t qt0, int32_t n_qt, int32_t n_kt,
