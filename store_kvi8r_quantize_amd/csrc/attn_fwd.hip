@@ -119,8 +119,8 @@ struct Stage {
 // as 0 through the buffer range check.  K and V parts can be fetched separately.
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
-  const int64_t row0 = (int64_t)kt * kTile;
-  const int64_t left = a.s_kv - row0;  // >= 1
+  const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
+  const int64_t left = a.s_kv - row0;  // >= 1, or 0 for an empty store (every load then reads 0)
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;  // bytes between tokens
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
@@ -148,8 +148,8 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
 
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
-  const int64_t row0 = (int64_t)kt * kTile;
-  const int64_t left = a.s_kv - row0;  // >= 1
+  const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
+  const int64_t left = a.s_kv - row0;  // >= 1, or 0 for an empty store (every load then reads 0)
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
