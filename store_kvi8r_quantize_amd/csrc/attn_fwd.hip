@@ -289,12 +289,10 @@ struct RowBlock {
 };
 
 // lk points at this lane's K row c, dims 8g.. of the current buffer.  The two
-// 32-key chains are interleaved and each K fragment is read from LDS four
-// MFMAs ahead of its use.
+// 32-key chains are interleaved.
 template <int MODE>
-__device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
+__device__ __forceinline__ void qk_issue(RowBlock& rb, const uint16_t* lk) {
   using Op = Operand<MODE>;
-  constexpr int kAhead = 4;
   u32x4 ka[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) ka[i] = *reinterpret_cast<const u32x4*>(lk + 32 * (i & 1) * kKStride + 16 * (i >> 1));
@@ -306,22 +304,34 @@ __device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
   }
   rb.s[0] = s0;
   rb.s[1] = s1;
-  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+}
+
+// Issue order of 16 MFMAs and the LDS fragment reads feeding them: each read
+// runs kAhead MFMAs ahead of its use (RD reads per MFMA).
+template <int RD>
+__device__ __forceinline__ void mfma_read_pattern() {
+  constexpr int kAhead = 4;
+  __builtin_amdgcn_sched_group_barrier(0x100, RD * kAhead, 0);
 #pragma unroll
   for (int i = 0; i < 16 - kAhead; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+}
+
+template <int MODE>
+__device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
+  qk_issue<MODE>(rb, lk);
+  mfma_read_pattern<1>();
 }
 
 // O^T += V^T P^T.  k-step j covers keys 32*(j/2) + 16*(j%2) + 4g + {0..3} and
 // the same + 8, matching the order of the S^T accumulator registers in pf.
 // lv points at this lane's V^T row c, keys 4g.. of the current buffer.
 template <int MODE>
-__device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
+__device__ __forceinline__ void pv_issue(RowBlock& rb, const uint16_t* lv) {
   using Op = Operand<MODE>;
-  constexpr int kAhead = 4;
   u32x4 va[16];  // k-step major, so the four accumulator chains interleave
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -336,13 +346,12 @@ __device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
     const int j = i >> 2, db = i & 3;
     rb.acc[db] = Op::mfma(va[i], rb.pf[j >> 1][j & 1], rb.acc[db]);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-#pragma unroll
-  for (int i = 0; i < 16 - kAhead; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
+}
+
+template <int MODE>
+__device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
+  pv_issue<MODE>(rb, lv);
+  mfma_read_pattern<2>();
 }
 
 // Score factors of this lane's keys 32*kb + 8*jg + 4g + {0..3}: key scale *
@@ -391,15 +400,14 @@ __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float 
   }
 }
 
-// Online softmax of one tile.  Exponentials are taken against the running max
-// already held (one fma each).  Only when the row's tile sum of p exceeds 2^8
-// (so that no p can exceed 2^8 otherwise; always true on the first tile, where
-// the running max is -inf) does the row take the tile max as its new running
-// max, rescale O and l, and redo the tile.  A sum above 2^8 implies some p
-// above 2^3, so the new max is always above the old one.
 template <int MODE, bool PARTIAL>
-__device__ __forceinline__ void softmax_block(RowBlock& rb, const float* lc, float sl2, int n_valid, int g) {
-  float lsum = tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g);
+__device__ __forceinline__ float softmax_fast(RowBlock& rb, const float* lc, float sl2, int n_valid, int g) {
+  return tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g);
+}
+
+template <int MODE, bool PARTIAL>
+__device__ __forceinline__ void softmax_finish(RowBlock& rb, float lsum, const float* lc, float sl2, int n_valid,
+                                               int g) {
   if (!(pair_max(lsum) <= kLazyBound)) {
     float mx = -__builtin_inff();
 #pragma unroll
@@ -421,6 +429,17 @@ __device__ __forceinline__ void softmax_block(RowBlock& rb, const float* lc, flo
     lsum = tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g);
   }
   rb.l += lsum;
+}
+
+// Online softmax of one tile.  Exponentials are taken against the running max
+// already held (one fma each).  Only when the row's tile sum of p exceeds 2^8
+// (so that no p can exceed 2^8 otherwise; always true on the first tile, where
+// the running max is -inf) does the row take the tile max as its new running
+// max, rescale O and l, and redo the tile.  A sum above 2^8 implies some p
+// above 2^3, so the new max is always above the old one.
+template <int MODE, bool PARTIAL>
+__device__ __forceinline__ void softmax_block(RowBlock& rb, const float* lc, float sl2, int n_valid, int g) {
+  softmax_finish<MODE, PARTIAL>(rb, softmax_fast<MODE, PARTIAL>(rb, lc, sl2, n_valid, g), lc, sl2, n_valid, g);
 }
 
 // Normalise and store this lane's 64 dims of its query row.
