@@ -18,11 +18,13 @@ fp64 NumPy throughout, per-head processing.  What it follows:
   options": scores are invariant under the rotation, P.V is brought back
   through the transpose once; fp16 rather than bf16 inside kvi8r.
 * "H3-Optimizations" page, Nodes (H3 Sparse Attention and the routed-geometry
-  paragraph): 64Q x 64KV tiles, the hard arm drops rejected tiles.
+  paragraph): 64Q x 64KV tiles, the hard arm drops rejected tiles, the Sol arm
+  stands in for them with block-mean K and block-sum V.
 
 Modules: ``hadamard`` (the basis), ``encodings`` (exact bf16/fp16 decoding and
 fp16 rounding), ``kvi8r`` (quantise / dequantise), ``attention`` (exact, kvi8r,
-tile-masked and blockwise log-sum-exp attention).
+tile-masked and blockwise log-sum-exp attention), ``sol`` (tile-masked
+attention with the dropped tiles' block-mean residual).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, brute force and an independent library
@@ -33,10 +35,12 @@ from .encodings import bf16_to_f64, f16_to_f64, f64_to_f16_bits
 from .kvi8r import rotate_rows, row_scales, codes_for_scales, quantize_rows, dequantize_rows
 from .attention import (attention, attention_blockwise, kvi8r_attention, expand_tile_mask,
                         exact_attention_bf16)
+from .sol import tile_summaries, sol_attention, exact_sol_attention_bf16, kvi8r_sol_attention
 
 __all__ = [
     "sylvester_hadamard", "orthonormal_hadamard", "bf16_to_f64", "f16_to_f64", "f64_to_f16_bits",
     "rotate_rows", "row_scales", "codes_for_scales", "quantize_rows", "dequantize_rows",
     "attention", "attention_blockwise", "kvi8r_attention", "expand_tile_mask",
+    "tile_summaries", "sol_attention", "exact_sol_attention_bf16", "kvi8r_sol_attention",
     "exact_attention_bf16",
 ]
