@@ -54,6 +54,13 @@ extern "C" {
 #define H3A_MODE_EXACT_BF16 0 /* "bf16 (exact)": K/V kept as bf16, stock attention math */
 #define H3A_MODE_KVI8R 1      /* "kvi8r": rotated int8 K/V with one fp16 scale per (token, head) row */
 
+/* Flag OR-ed into mode (with a tile_mask only): every dropped KV tile still
+ * contributes, as one pseudo-key -- its block-mean key with its block-mean value,
+ * counted as many times as the tile has keys -- instead of being left out of the
+ * softmax (the Sol arm, which stands in for rejected tiles with block-mean K and
+ * block-sum V [P3 Nodes, routed geometry]). */
+#define H3A_SOL 0x100
+
 /* ABI version of the loaded library; callers compare it with H3A_ABI_VERSION. */
 int32_t h3a_abi_version(void);
 
@@ -90,7 +97,9 @@ int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens,
 
 /*
  * h3a_attention_workspace_bytes -- bytes of workspace h3a_attention needs.
- * sparse != 0 when a tile_mask will be passed.  Returns 0 when none is needed.
+ * sparse != 0 when a tile_mask will be passed; mode as passed to h3a_attention
+ * (including H3A_SOL).  Returns 0 when none is needed or the arguments are
+ * invalid.
  */
 size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim,
                                      int64_t q_chunk, int32_t mode, int32_t sparse);
@@ -102,6 +111,7 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
  *
  *   O[t, h, :] = sum_j softmax_j(softmax_scale * q[t,h,:] . k[j,h,:]) v[j,h,:]
  *
+ * mode is H3A_MODE_EXACT_BF16 or H3A_MODE_KVI8R, optionally OR-ed with H3A_SOL.
  * mode H3A_MODE_EXACT_BF16: k_store / v_store are bf16 [s_kv, n_heads, 128]
  *   (token-major), scales must be NULL.  Inputs feed bf16 matrix cores, fp32
  *   accumulation.  The output is bitwise identical for every q_chunk and
@@ -125,6 +135,15 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
  *             ceil(s_kv/64)]: entry != 0 keeps the 64-query x 64-key tile, 0
  *             drops it from the softmax (hard arm).  A query row with no kept
  *             key gets an all-zero output, as does every row when s_kv == 0.
+ *             With mode | H3A_SOL, a dropped tile t of n_t keys adds one
+ *             pseudo-key instead: the mean of its keys, with the mean of its
+ *             values, at softmax weight n_t * exp(scale * q . mean key).  The
+ *             means are taken once per call over the dequantised store in fp32
+ *             and rounded to the matrix-core input type (fp16 for kvi8r, bf16
+ *             for exact); the mean key is first scaled by a power of two, an
+ *             exact step that keeps it inside the fp16 range.  A query row whose
+ *             tiles are all dropped attends the pseudo-keys alone.  H3A_SOL
+ *             without a tile_mask, or with s_kv > 2^30 - 64, is H3A_EINVAL.
  * workspace:  at least h3a_attention_workspace_bytes(...) bytes of device
  *             memory, 256-byte aligned (may be NULL when that is 0).
  */

@@ -25,6 +25,7 @@ TILE = 64
 MODE_EXACT_BF16 = 0
 MODE_KVI8R = 1
 MODES = {"exact": MODE_EXACT_BF16, "bf16": MODE_EXACT_BF16, "kvi8r": MODE_KVI8R}
+SOL = 0x100  # H3A_SOL: dropped tiles of a tile_mask enter as one pseudo-key each
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libh3a.so")
 
@@ -131,22 +132,25 @@ def new_kvi8r_store(s_total: int, n_heads: int, device="cuda"):
 
 
 def h3a_attention_workspace_bytes(s_q: int, s_kv: int, n_heads: int, q_chunk: int, mode, sparse: bool,
-                                  head_dim: int = HEAD_DIM) -> int:
-    mode = MODES.get(mode, mode)
-    return int(_load().h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, int(mode), int(sparse)))
+                                  head_dim: int = HEAD_DIM, sol: bool = False) -> int:
+    mode = int(MODES.get(mode, mode)) | (SOL if sol else 0)
+    return int(_load().h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, mode, int(sparse)))
 
 
 def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: int = 0, mode="kvi8r",
-                  tile_mask=None, softmax_scale: float | None = None, workspace=None, stream=None):
+                  tile_mask=None, sol: bool = False, softmax_scale: float | None = None, workspace=None,
+                  stream=None):
     """Chunked attention of q (bf16 [s_q, H, 128]) against a K/V store, written into out (bf16 [s_q, H, 128]).
 
     mode "exact": k_store / v_store bf16 [s_kv, H, 128], scales None.
     mode "kvi8r": k_store / v_store int8 [H, s_kv, 128], scales fp16 [2, H, s_kv].
     tile_mask: None (dense) or uint8 [H, ceil(s_q/64), ceil(s_kv/64)].
+    sol: with a tile_mask, each dropped tile enters as one pseudo-key (tile-mean K and V, weight = its key count).
     workspace: a uint8 GPU tensor of at least h3a_attention_workspace_bytes; allocated here when None.
     """
     lib = _load()
     mode = MODES.get(mode, mode)
+    flags = SOL if sol else 0
     _need(q, "q", torch.bfloat16)
     _need(out, "out", torch.bfloat16)
     if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
@@ -170,13 +174,13 @@ def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: i
             raise ValueError("tile_mask must be contiguous")
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
-    need = int(lib.h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, int(mode),
+    need = int(lib.h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, int(mode) | flags,
                                                  int(tile_mask is not None)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.h3a_attention(_ptr(q), _ptr(k_store), _ptr(v_store), _ptr(scales), s_q, s_kv, n_heads, head_dim,
-                             float(softmax_scale), int(q_chunk), int(kv_block), int(mode), _ptr(tile_mask),
+                             float(softmax_scale), int(q_chunk), int(kv_block), int(mode) | flags, _ptr(tile_mask),
                              _ptr(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
     return out
 

@@ -276,6 +276,61 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
   store_tile_v<MODE, NT>(st, lv, tid);
 }
 
+// Pseudo-key tile of the Sol residual ("H3-Optimizations" page, Nodes, routed
+// geometry: a rejected tile is stood in for by its block-mean K and block-sum
+// V).  Slot s < n_valid holds dropped KV tile dl[s] as one key, its tile-mean
+// key divided by kmscale, with its tile-mean value; the other slots hold
+// zeros.  lc[s] = kmscale * softmax_scale * log2 e and lc[kTile + s] = log2 of
+// the tile's key count, so the key's weight is count * exp(scale * q . mean).
+// First the slots' tile indices go to lt (-1 = empty), then every thread
+// fetches its K and V^T pieces with buffer loads at 32-bit offsets from the
+// head's tables (an empty slot's offset is past the table end and reads 0).
+template <int NT>
+__device__ __forceinline__ void stage_pseudo_tile(const AttnChunk& a, const SolArgs& sa, const int32_t* dl,
+                                                  int n_valid, int head, int n_kt, uint16_t* lk, uint16_t* lv,
+                                                  float* lc, int32_t* lt, float sl2, int tid) {
+  const int64_t hbase = (int64_t)head * n_kt;
+  if (tid < kTile) {
+    float f = 0.0f, b = 0.0f;
+    int t = -1;
+    if (tid < n_valid) {
+      t = dl[tid];
+      const int64_t cnt = a.s_kv - (int64_t)t * kTile;
+      f = sa.kmscale[hbase + t] * sl2;
+      b = log2f((float)(cnt < kTile ? cnt : kTile));
+    }
+    lc[tid] = f;
+    lc[kTile + tid] = b;
+    lt[tid] = t;
+  }
+  __syncthreads();
+  const uint32_t table = (uint32_t)n_kt * (kHeadDim * 2);  // bytes per head (< 2^32)
+  const auto rk = make_rsrc(sa.kmean + hbase * kHeadDim, table);
+  const auto rv = make_rsrc(sa.vmean + hbase * kHeadDim, table);
+#pragma unroll
+  for (int j = 0; j < 512 / NT; ++j) {  // K: unit = one slot x 16 dims
+    const int u = tid + NT * j;
+    const int r = u >> 3, d16 = u & 7;
+    const int t = lt[r];
+    const uint32_t o = t >= 0 ? (uint32_t)t * (kHeadDim * 2) + 32 * d16 : table;
+    const u32x4 c0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+    const u32x4 c1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o + 16, 0, 0));
+    *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16) = c0;
+    *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
+  }
+#pragma unroll
+  for (int j = 0; j < 1024 / NT; ++j) {  // V^T: unit = one slot x 8 dims, written element by element
+    const int u = tid + NT * j;
+    const int r = u & 63, d8 = u >> 6;
+    const int t = lt[r];
+    const uint32_t o = t >= 0 ? (uint32_t)t * (kHeadDim * 2) + 16 * d8 : table;
+    const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      lv[(8 * d8 + i) * kVStride + r] = (uint16_t)((i & 1) ? w[i >> 1] >> 16 : w[i >> 1] & 0xFFFFu);
+  }
+}
+
 // State of one 32-query block of a wave: its rows are lanes c = 0..31 (both
 // halves g = 0, 1 of the wave hold the same query, different keys / dims).
 struct RowBlock {
@@ -356,18 +411,24 @@ __device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
 
 // Score factors of this lane's keys 32*kb + 8*jg + 4g + {0..3}: key scale *
 // softmax_scale * log2 e (kvi8r, from LDS) or softmax_scale * log2 e (exact).
-template <int MODE>
+// Pseudo-key tiles (Sol residual) take theirs from LDS in both modes, and also
+// a per-key additive term, log2 of the key's multiplicity, from lc + kTile.
+template <int MODE, bool PSEUDO = false>
 __device__ __forceinline__ u32x4 score_factors(const float* lc, float sl2, int kb, int jg, int g) {
-  if constexpr (MODE == 1) return *reinterpret_cast<const u32x4*>(lc + 32 * kb + 8 * jg + 4 * g);
+  if constexpr (MODE == 1 || PSEUDO) return *reinterpret_cast<const u32x4*>(lc + 32 * kb + 8 * jg + 4 * g);
   const uint32_t f = __float_as_uint(sl2);
   return u32x4{f, f, f, f};
+}
+__device__ __forceinline__ u32x4 score_bias(const float* lc, int kb, int jg, int g) {
+  return *reinterpret_cast<const u32x4*>(lc + kTile + 32 * kb + 8 * jg + 4 * g);
 }
 
 // p = exp2(s * factor - m) for this lane's 32 keys, packed into pf; returns the
 // sum of this lane's p in a fixed order.  kvi8r sums the fp16-rounded P with
 // packed fp16 adds (pairs, then a tree); exact sums the fp32 p in a tree.  Row
 // sums avoid v_dot2: it runs on the matrix pipeline and stalls next to MFMA.
-template <int MODE, bool PARTIAL>
+// PSEUDO adds each key's log2 multiplicity to its exponent.
+template <int MODE, bool PARTIAL, bool PSEUDO = false>
 __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float sl2, float nm, int n_valid, int g) {
   using Op = Operand<MODE>;
   float gs[8];     // exact: sum of each group of 4
@@ -376,11 +437,12 @@ __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float 
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
-      const u32x4 cc = score_factors<MODE>(lc, sl2, kb, jg, g);
+      const u32x4 cc = score_factors<MODE, PSEUDO>(lc, sl2, kb, jg, g);
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = __builtin_fmaf(rb.s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
+        if constexpr (PSEUDO) x += __uint_as_float(score_bias(lc, kb, jg, g)[e]);
         if constexpr (PARTIAL) x = 32 * kb + 8 * jg + 4 * g + e < n_valid ? x : -__builtin_inff();
         p[e] = __builtin_amdgcn_exp2f(x);
       }
@@ -400,12 +462,12 @@ __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float 
   }
 }
 
-template <int MODE, bool PARTIAL>
+template <int MODE, bool PARTIAL, bool PSEUDO = false>
 __device__ __forceinline__ float softmax_fast(RowBlock& rb, const float* lc, float sl2, int n_valid, int g) {
-  return tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g);
+  return tile_exps<MODE, PARTIAL, PSEUDO>(rb, lc, sl2, -rb.m, n_valid, g);
 }
 
-template <int MODE, bool PARTIAL>
+template <int MODE, bool PARTIAL, bool PSEUDO = false>
 __device__ __forceinline__ void softmax_finish(RowBlock& rb, float lsum, const float* lc, float sl2, int n_valid,
                                                int g) {
   if (!(pair_max(lsum) <= kLazyBound)) {
@@ -414,11 +476,14 @@ __device__ __forceinline__ void softmax_finish(RowBlock& rb, float lsum, const f
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int jg = 0; jg < 4; ++jg) {
-        const u32x4 cc = score_factors<MODE>(lc, sl2, kb, jg, g);
+        const u32x4 cc = score_factors<MODE, PSEUDO>(lc, sl2, kb, jg, g);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (!PARTIAL || 32 * kb + 8 * jg + 4 * g + e < n_valid)
-            mx = fmaxf(mx, rb.s[kb][4 * jg + e] * __uint_as_float(cc[e]));
+          if (!PARTIAL || 32 * kb + 8 * jg + 4 * g + e < n_valid) {
+            float x = rb.s[kb][4 * jg + e] * __uint_as_float(cc[e]);
+            if constexpr (PSEUDO) x += __uint_as_float(score_bias(lc, kb, jg, g)[e]);
+            mx = fmaxf(mx, x);
+          }
       }
     mx = pair_max(mx);
     const float alpha = __builtin_amdgcn_exp2f(rb.m - mx);
@@ -426,7 +491,7 @@ __device__ __forceinline__ void softmax_finish(RowBlock& rb, float lsum, const f
     for (int i = 0; i < 4; ++i) rb.acc[i] *= alpha;
     rb.l *= alpha;
     rb.m = mx;
-    lsum = tile_exps<MODE, PARTIAL>(rb, lc, sl2, -rb.m, n_valid, g);
+    lsum = tile_exps<MODE, PARTIAL, PSEUDO>(rb, lc, sl2, -rb.m, n_valid, g);
   }
   rb.l += lsum;
 }
@@ -437,9 +502,10 @@ __device__ __forceinline__ void softmax_finish(RowBlock& rb, float lsum, const f
 // the running max is -inf) does the row take the tile max as its new running
 // max, rescale O and l, and redo the tile.  A sum above 2^8 implies some p
 // above 2^3, so the new max is always above the old one.
-template <int MODE, bool PARTIAL>
+template <int MODE, bool PARTIAL, bool PSEUDO = false>
 __device__ __forceinline__ void softmax_block(RowBlock& rb, const float* lc, float sl2, int n_valid, int g) {
-  softmax_finish<MODE, PARTIAL>(rb, softmax_fast<MODE, PARTIAL>(rb, lc, sl2, n_valid, g), lc, sl2, n_valid, g);
+  softmax_finish<MODE, PARTIAL, PSEUDO>(rb, softmax_fast<MODE, PARTIAL, PSEUDO>(rb, lc, sl2, n_valid, g), lc, sl2,
+                                        n_valid, g);
 }
 
 // Normalise and store this lane's 64 dims of its query row.
@@ -472,15 +538,16 @@ __device__ __forceinline__ void store_rows(const RowBlock& rb, const AttnChunk& 
 // wave let four workgroups share a CU, two waves per SIMD, so one workgroup's
 // staging and softmax run under another's matrix-core work.  Per kept tile:
 //     stage(i) [barrier] fetch(i+1), QK(i), softmax(i), PV(i) [barrier]
-// Each row's arithmetic is that of the dense kernel.
-template <int MODE>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_fwd_sparse_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
+// Each row's arithmetic is that of the dense kernel.  With SOL, the dropped
+// tiles then follow as pseudo-keys, 64 per pass (stage_pseudo_tile).
+// lds_k, lds_v: one K and one V^T tile; lds_c: score factors, with SOL followed
+// by the pseudo slots' biases and tile indices.
+template <int MODE, bool SOL>
+__device__ __forceinline__ void attn_fwd_sparse_body(const AttnChunk& a, int32_t n_qt, int32_t n_kt,
+                                                     const SolArgs& sa, uint16_t* lds_k, uint16_t* lds_v,
+                                                     float* lds_c) {
   constexpr int NT = 128;
   constexpr int BM = 64;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kKTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kVTileElems];
-  __shared__ __attribute__((aligned(16))) float lds_c[kTile];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -548,7 +615,40 @@ void attn_fwd_sparse_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
     softmax_block<MODE, true>(rb, lds_c, sl2, n_valid, g);
     pv_block<MODE>(rb, lv);
   }
+  if constexpr (SOL) {
+    const int n_drop = n_kt - n_tiles;
+    const int32_t* dl = sa.drops + ((int64_t)head * n_qt + qt) * n_kt;
+    for (int p0 = 0; p0 < n_drop; p0 += kTile) {
+      __syncthreads();  // both waves are done with the tile in LDS
+      const int nv = n_drop - p0 < kTile ? n_drop - p0 : kTile;
+      stage_pseudo_tile<NT>(a, sa, dl + p0, nv, head, n_kt, lds_k, lds_v, lds_c,
+                            reinterpret_cast<int32_t*>(lds_c + 2 * kTile), sl2, tid);
+      __syncthreads();
+      qk_block<MODE>(rb, lk);
+      softmax_block<MODE, true, true>(rb, lds_c, sl2, nv, g);
+      pv_block<MODE>(rb, lv);
+    }
+  }
   store_rows<MODE>(rb, a, head, g);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_sparse_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kKTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kVTileElems];
+  __shared__ __attribute__((aligned(16))) float lds_c[kTile];
+  attn_fwd_sparse_body<MODE, false>(a, n_qt, n_kt, SolArgs{}, lds_k, lds_v, lds_c);
+}
+
+// The same with the Sol residual: dropped tiles enter as pseudo-keys.
+template <int MODE>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_sparse_sol_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt, SolArgs sa) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kKTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[kVTileElems];
+  __shared__ __attribute__((aligned(16))) float lds_c[3 * kTile];
+  attn_fwd_sparse_body<MODE, true>(a, n_qt, n_kt, sa, lds_k, lds_v, lds_c);
 }
 
 // Dense kernel: 8 waves x 32 query rows = 256 rows of one head, two waves per
@@ -673,11 +773,13 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
   store_rows<MODE>(rb, a, head, g);
 }
 
-// Kept-tile list of one (head, q-tile) row of the mask, in increasing key order.
+// Kept-tile list of one (head, q-tile) row of the mask, in increasing key
+// order; with drops, also the list of the dropped tiles, in increasing order.
 __global__ __launch_bounds__(256) void route_build_kernel(const uint8_t* __restrict__ mask, int64_t n_qt_total,
                                                           int64_t qt0, int32_t n_qt, int32_t n_kt,
                                                           int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ lists) {
+                                                          int32_t* __restrict__ lists,
+                                                          int32_t* __restrict__ drops) {
   __shared__ int part[256];
   const int qt = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
   const uint8_t* row = mask + ((int64_t)head * n_qt_total + qt0 + qt) * n_kt;
@@ -697,17 +799,80 @@ __global__ __launch_bounds__(256) void route_build_kernel(const uint8_t* __restr
   int32_t* out = lists + ((int64_t)head * n_qt + qt) * n_kt;
   for (int j = b0; j < b1; ++j)
     if (row[j]) out[pos++] = j;
+  if (drops != nullptr) {
+    int dpos = b0 - (part[tid] - cnt);  // tiles before b0 that are dropped
+    int32_t* dout = drops + ((int64_t)head * n_qt + qt) * n_kt;
+    for (int j = b0; j < b1; ++j)
+      if (!row[j]) dout[dpos++] = j;
+  }
   if (tid == 255) counts[head * n_qt + qt] = part[255];
 }
 
+// Tile means for the Sol residual: one workgroup per (KV tile, head); threads
+// 0-127 average the tile's keys and 128-255 its values, dimension by
+// dimension, in fp32 over the dequantised store (a kvi8r code times its fp16
+// scale is exact in fp32).  The mean value is rounded to the matrix-core type.
+// The mean key is first divided by a power of two 2^e chosen so that its
+// largest magnitude lies in [64, 128) -- an exact step -- then rounded, which
+// keeps fp16 from overflowing on large keys; 2^e goes to kmscale.
 template <int MODE>
-hipError_t launch_sparse(const AttnChunk& a, hipStream_t stream) {
+__global__ __launch_bounds__(256) void tile_means_kernel(const void* __restrict__ k, const void* __restrict__ v,
+                                                         const uint16_t* __restrict__ k_scale,
+                                                         const uint16_t* __restrict__ v_scale, int64_t s_kv,
+                                                         int32_t n_heads, uint16_t* __restrict__ kmean,
+                                                         uint16_t* __restrict__ vmean, float* __restrict__ kmscale) {
+  __shared__ float wmax[2];
+  const int t = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
+  const int n_kt = (int)gridDim.x;
+  const int d = tid & (kHeadDim - 1);
+  const bool is_v = tid >= kHeadDim;
+  const int64_t r0 = (int64_t)t * kTile;
+  const int n = (int)(s_kv - r0 < kTile ? s_kv - r0 : kTile);  // >= 1
+  float sum = 0.0f;
+  if constexpr (MODE == 0) {
+    const uint16_t* src = static_cast<const uint16_t*>(is_v ? v : k) + (r0 * n_heads + head) * kHeadDim + d;
+    for (int r = 0; r < n; ++r) sum += bf16lo_to_f32(src[(int64_t)r * n_heads * kHeadDim]);
+  } else {
+    const int64_t hr = (int64_t)head * s_kv + r0;
+    const int8_t* src = static_cast<const int8_t*>(is_v ? v : k) + hr * kHeadDim + d;
+    const uint16_t* sc = (is_v ? v_scale : k_scale) + hr;
+    for (int r = 0; r < n; ++r)
+      sum += (float)src[(int64_t)r * kHeadDim] * (float)__builtin_bit_cast(_Float16, sc[r]);
+  }
+  const float mean = sum / (float)n;
+  const int64_t o = ((int64_t)head * n_kt + t) * kHeadDim + d;
+  if (is_v) vmean[o] = (uint16_t)(Operand<MODE>::pack(mean, 0.0f) & 0xFFFFu);
+  float amax = fabsf(mean);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (!is_v && (tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  if (!is_v) {
+    const float mx = fmaxf(wmax[0], wmax[1]);
+    int e = 0;
+    if (mx > 0.0f) (void)frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
+    kmean[o] = (uint16_t)(Operand<MODE>::pack(ldexpf(mean, 7 - e), 0.0f) & 0xFFFFu);
+    if (tid == 0) kmscale[(int64_t)head * n_kt + t] = ldexpf(1.0f, e - 7);
+  }
+}
+
+template <int MODE, bool SOL>
+hipError_t launch_sparse(const AttnChunk& a, const SolArgs& sa, hipStream_t stream) {
   const int32_t n_qt = (int32_t)((a.rows + kSparseBlockRows - 1) / kSparseBlockRows);
   const int32_t n_kt = (int32_t)((a.s_kv + kTile - 1) / kTile);
   const int64_t n_wg = (int64_t)n_qt * a.n_heads;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_fwd_sparse_kernel<MODE>), dim3((unsigned)n_wg), dim3(128), 0, stream, a, n_qt, n_kt);
+  if constexpr (SOL)
+    hipLaunchKernelGGL((attn_fwd_sparse_sol_kernel<MODE>), dim3((unsigned)n_wg), dim3(128), 0, stream, a, n_qt,
+                       n_kt, sa);
+  else
+    hipLaunchKernelGGL((attn_fwd_sparse_kernel<MODE>), dim3((unsigned)n_wg), dim3(128), 0, stream, a, n_qt, n_kt);
   return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_sparse(const AttnChunk& a, const SolArgs* sol, hipStream_t stream) {
+  return sol != nullptr ? launch_sparse<MODE, true>(a, *sol, stream) : launch_sparse<MODE, false>(a, SolArgs{}, stream);
 }
 
 }  // namespace
@@ -722,17 +887,34 @@ hipError_t launch_dense(const AttnChunk& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, hipStream_t stream) {
+hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, const SolArgs* sol, hipStream_t stream) {
   static_assert(kSparseBlockRows == 2 * 32, "sparse kernel covers one routing tile");
-  if (mode == 0) return sparse ? launch_sparse<0>(a, stream) : launch_dense<0>(a, stream);
-  return sparse ? launch_sparse<1>(a, stream) : launch_dense<1>(a, stream);
+  if (sol != nullptr && (!sparse || a.s_kv > kSolMaxKv)) return hipErrorInvalidValue;
+  if (mode == 0) return sparse ? launch_sparse<0>(a, sol, stream) : launch_dense<0>(a, stream);
+  return sparse ? launch_sparse<1>(a, sol, stream) : launch_dense<1>(a, stream);
 }
 
 hipError_t launch_route_build(const uint8_t* mask, int64_t n_qt_total, int64_t qt0, int32_t n_qt, int32_t n_kt,
-                              int32_t n_heads, int32_t* counts, int32_t* lists, hipStream_t stream) {
+                              int32_t n_heads, int32_t* counts, int32_t* lists, int32_t* drops,
+                              hipStream_t stream) {
   if (n_qt == 0) return hipSuccess;
   hipLaunchKernelGGL(route_build_kernel, dim3((unsigned)n_qt, (unsigned)n_heads), dim3(256), 0, stream, mask,
-                     n_qt_total, qt0, n_qt, n_kt, counts, lists);
+                     n_qt_total, qt0, n_qt, n_kt, counts, lists, drops);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_means(int mode, const void* k, const void* v, const uint16_t* k_scale,
+                             const uint16_t* v_scale, int64_t s_kv, int32_t n_heads, uint16_t* kmean,
+                             uint16_t* vmean, float* kmscale, hipStream_t stream) {
+  const int64_t n_kt = (s_kv + kTile - 1) / kTile;
+  if (n_kt == 0) return hipSuccess;
+  const dim3 grid((unsigned)n_kt, (unsigned)n_heads);
+  if (mode == 0)
+    hipLaunchKernelGGL(tile_means_kernel<0>, grid, dim3(256), 0, stream, k, v, k_scale, v_scale, s_kv, n_heads,
+                       kmean, vmean, kmscale);
+  else
+    hipLaunchKernelGGL(tile_means_kernel<1>, grid, dim3(256), 0, stream, k, v, k_scale, v_scale, s_kv, n_heads,
+                       kmean, vmean, kmscale);
   return hipGetLastError();
 }
 

@@ -71,18 +71,32 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 struct WorkspaceLayout {
-  uint64_t qrot = 0, orot = 0, counts = 0, lists = 0, total = 0;
+  uint64_t kmean = 0, vmean = 0, kmscale = 0;  // whole call (Sol)
+  uint64_t qrot = 0, orot = 0, counts = 0, lists = 0, drops = 0, total = 0;  // one query chunk
 };
 
-// Workspace per query chunk: rotated Q (fp16), rotated output (fp32), sparse kept lists.
+// Workspace: Sol tile means of the store (once per call), then per query chunk
+// rotated Q (fp16), rotated output (fp32), sparse kept (and Sol dropped) lists.
+// mode is the base mode; sol needs sparse.
 bool workspace_layout(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chunk, int32_t mode, bool sparse,
-                      WorkspaceLayout* w) {
+                      bool sol, WorkspaceLayout* w) {
   *w = WorkspaceLayout{};
   if (s_q <= 0 || q_chunk <= 0) return true;
   const int64_t rows = q_chunk < s_q ? q_chunk : s_q;
   int64_t elems;
   if (!mul_ok(rows, (int64_t)n_heads * H3A_HEAD_DIM, &elems)) return false;
   uint64_t off = 0;
+  if (sol) {
+    const int64_t n_kt = (s_kv + H3A_TILE - 1) / H3A_TILE;
+    int64_t nm;
+    if (!mul_ok(n_kt * n_heads, H3A_HEAD_DIM, &nm)) return false;
+    w->kmean = off;
+    off = align256(off + (uint64_t)nm * 2);
+    w->vmean = off;
+    off = align256(off + (uint64_t)nm * 2);
+    w->kmscale = off;
+    off = align256(off + (uint64_t)(n_kt * n_heads) * 4);
+  }
   if (mode == H3A_MODE_KVI8R) {
     w->qrot = off;
     off = align256(off + (uint64_t)elems * 2);
@@ -98,6 +112,10 @@ bool workspace_layout(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chun
     off = align256(off + (uint64_t)nc * 4);
     w->lists = off;
     off = align256(off + (uint64_t)nl * 4);
+    if (sol) {
+      w->drops = off;
+      off = align256(off + (uint64_t)nl * 4);
+    }
   }
   w->total = off;
   return true;
@@ -149,8 +167,11 @@ int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens,
 size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, int64_t q_chunk,
                                      int32_t mode, int32_t sparse) {
   if (head_dim != H3A_HEAD_DIM || n_heads < 1 || s_kv < 0) return 0;
+  const bool sol = (mode & H3A_SOL) != 0;
+  mode &= ~H3A_SOL;
+  if ((mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R) || (sol && !sparse)) return 0;
   WorkspaceLayout w;
-  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse != 0, &w)) return 0;
+  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse != 0, sol, &w)) return 0;
   return (size_t)w.total;
 }
 
@@ -160,7 +181,12 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
                       size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
-  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R) return fail(H3A_EINVAL, "unknown mode %d", mode);
+  const bool sol = (mode & H3A_SOL) != 0;
+  const int32_t mode_arg = mode;
+  mode &= ~H3A_SOL;
+  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R) return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
+  if (sol && tile_mask == nullptr) return fail(H3A_EINVAL, "H3A_SOL needs a tile_mask");
+  if (sol && s_kv > h3a::kSolMaxKv) return fail(H3A_EINVAL, "H3A_SOL supports s_kv up to 2^30 - 64");
   if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
   if (s_q < 0 || s_kv < 0) return fail(H3A_EINVAL, "s_q and s_kv must be >= 0");
   if (s_q > ((int64_t)1 << 31) || s_kv > ((int64_t)1 << 31)) return fail(H3A_EINVAL, "sequence too long");
@@ -195,7 +221,8 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
     if ((rc = check_buffer(tile_mask, (uint64_t)mb, 1, "tile_mask")) != H3A_OK) return rc;
   }
   WorkspaceLayout wl;
-  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse, &wl)) return fail(H3A_EINVAL, "size overflow");
+  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse, sol, &wl))
+    return fail(H3A_EINVAL, "size overflow");
   if (wl.total > 0) {
     if (workspace == nullptr || workspace_bytes < wl.total)
       return fail(H3A_EWORKSPACE, "workspace needs %llu bytes (got %llu)", (unsigned long long)wl.total,
@@ -213,10 +240,21 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
     std::lock_guard<std::mutex> lk(g_timing_mu);
     timing = g_timing_on;
   }
+  const uint16_t* kv_scales = static_cast<const uint16_t*>(scales);
+  const uint16_t* k_scale = mode == H3A_MODE_KVI8R ? kv_scales : nullptr;
+  const uint16_t* v_scale = mode == H3A_MODE_KVI8R ? kv_scales + s_kv * n_heads : nullptr;
+  if (sol) {
+    hipError_t e = h3a::launch_tile_means(mode, k_store, v_store, k_scale, v_scale, s_kv, n_heads,
+                                          reinterpret_cast<uint16_t*>(ws + wl.kmean),
+                                          reinterpret_cast<uint16_t*>(ws + wl.vmean),
+                                          reinterpret_cast<float*>(ws + wl.kmscale), st);
+    if (e != hipSuccess) return hip_fail(e, "tile_means launch");
+  }
   for (int64_t c0 = 0; c0 < s_q; c0 += q_chunk) {
     const int64_t rows = (s_q - c0) < q_chunk ? (s_q - c0) : q_chunk;
     const int64_t off = c0 * n_heads * H3A_HEAD_DIM;
     h3a::AttnChunk a{};
+    h3a::SolArgs sa{};
     a.rows = rows;
     a.s_kv = s_kv;
     a.n_heads = n_heads;
@@ -229,8 +267,8 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
       if ((e = h3a::launch_rotate_q(qb + off, qrot, rows * n_heads, st)) != hipSuccess)
         return hip_fail(e, "rotate_q launch");
       a.q = qrot;
-      a.k_scale = static_cast<const uint16_t*>(scales);
-      a.v_scale = static_cast<const uint16_t*>(scales) + s_kv * n_heads;
+      a.k_scale = k_scale;
+      a.v_scale = v_scale;
       a.out = ws + wl.orot;
     } else {
       a.q = qb + off;
@@ -239,10 +277,18 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
     if (sparse) {
       a.counts = reinterpret_cast<const int32_t*>(ws + wl.counts);
       a.lists = reinterpret_cast<const int32_t*>(ws + wl.lists);
+      int32_t* drops = nullptr;
+      if (sol) {
+        drops = reinterpret_cast<int32_t*>(ws + wl.drops);
+        sa.drops = drops;
+        sa.kmean = reinterpret_cast<const uint16_t*>(ws + wl.kmean);
+        sa.vmean = reinterpret_cast<const uint16_t*>(ws + wl.vmean);
+        sa.kmscale = reinterpret_cast<const float*>(ws + wl.kmscale);
+      }
       const int32_t n_qt = (int32_t)((rows + H3A_TILE - 1) / H3A_TILE);
       if ((e = h3a::launch_route_build(tile_mask, n_qt_total, c0 / H3A_TILE, n_qt, (int32_t)n_kt, n_heads,
                                        reinterpret_cast<int32_t*>(ws + wl.counts),
-                                       reinterpret_cast<int32_t*>(ws + wl.lists), st)) != hipSuccess)
+                                       reinterpret_cast<int32_t*>(ws + wl.lists), drops, st)) != hipSuccess)
         return hip_fail(e, "route_build launch");
     }
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -251,7 +297,8 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
         return hip_fail(e, "hipEventCreate");
       if ((e = hipEventRecord(ev0, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
-    if ((e = h3a::launch_attn_fwd(mode, sparse, a, st)) != hipSuccess) return hip_fail(e, "attn_fwd launch");
+    if ((e = h3a::launch_attn_fwd(mode, sparse, a, sol ? &sa : nullptr, st)) != hipSuccess)
+      return hip_fail(e, "attn_fwd launch");
     if (timing) {
       if ((e = hipEventRecord(ev1, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
       std::lock_guard<std::mutex> lk(g_timing_mu);

@@ -31,13 +31,34 @@ struct AttnChunk {
   float scale_log2;        // softmax_scale * log2(e)
 };
 
+// Sol residual of the sparse kernel: dropped tiles as pseudo-keys.
+struct SolArgs {
+  const int32_t* drops;    // dropped KV-tile indices [H, n_qtiles, n_kt], increasing; count = n_kt - kept
+  const uint16_t* kmean;   // per (head, KV tile): tile-mean key / kmscale, fp16 (kvi8r) or bf16 [H, n_kt, 128]
+  const uint16_t* vmean;   // per (head, KV tile): tile-mean value, same type [H, n_kt, 128]
+  const float* kmscale;    // per (head, KV tile): power-of-two scale of kmean [H, n_kt]
+};
+// Longest store with the Sol residual: the kernel addresses one head's mean
+// tables (n_kt rows of 256 bytes) with 32-bit offsets, one row past the end
+// included, so n_kt * 256 must stay below 2^32.
+constexpr int64_t kSolMaxKv = ((int64_t)1 << 30) - 64;
+
 constexpr int kSparseBlockRows = 64;  // q-tile of the sparse kernel = the routing granularity
 
-hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, hipStream_t stream);
+// sol: null, or the Sol residual (sparse only).
+hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, const SolArgs* sol, hipStream_t stream);
 
-// Kept-tile lists for the q-tiles [qt0, qt0 + n_qt) of every head.
+// Kept-tile lists (and, when drops is not null, dropped-tile lists) for the
+// q-tiles [qt0, qt0 + n_qt) of every head.
 hipError_t launch_route_build(const uint8_t* mask, int64_t n_qt_total, int64_t qt0, int32_t n_qt,
                               int32_t n_kt, int32_t n_heads, int32_t* counts, int32_t* lists,
-                              hipStream_t stream);
+                              int32_t* drops, hipStream_t stream);
+
+// Tile means of the whole store (Sol residual): kmean, vmean [H, n_kt, 128]
+// and kmscale [H, n_kt], as described in SolArgs.  k, v, k_scale, v_scale as
+// in AttnChunk for `mode`.
+hipError_t launch_tile_means(int mode, const void* k, const void* v, const uint16_t* k_scale,
+                             const uint16_t* v_scale, int64_t s_kv, int32_t n_heads, uint16_t* kmean,
+                             uint16_t* vmean, float* kmscale, hipStream_t stream);
 
 }  // namespace h3a

@@ -64,6 +64,10 @@ def _attn(lib, **kw):
     (dict(mask=1, q_chunk=100), -1, "multiple of 64"),
     (dict(mode=1, scales=None), -1, "scales"),
     (dict(mode=0, scales=16), -1, "no scales"),
+    (dict(mode=0x100 | 1, scales=16), -1, "H3A_SOL needs a tile_mask"),
+    (dict(mode=0x100 | 7, mask=1), -1, "mode"),
+    (dict(mode=0x200 | 1, mask=1, scales=16), -1, "mode"),
+    (dict(mode=0x100 | 1, mask=1, scales=16, s_kv=(1 << 30) - 63), -1, "2^30 - 64"),
 ])
 def test_attention_rejects_bad_arguments(lib, kw, status, msg):
     assert _attn(lib, **kw) == status
@@ -104,3 +108,9 @@ def test_workspace_sizes(lib):
     dense = h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "exact", True)
     assert dense >= 2 * 4 * 16 * 4 + 2 * 4 * 4
     assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "kvi8r", False, head_dim=64) == 0
+    # Sol: tile means of the store (K, V: [H, n_kt, 128] 16-bit; K scales: [H, n_kt] fp32) plus dropped lists
+    hard = h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, "exact", True)
+    sol = h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, "exact", True, sol=True)
+    n_kt = 16
+    assert sol >= hard + 2 * (2 * n_kt * 128 * 2) + 2 * n_kt * 4 + 2 * 4 * n_kt * 4
+    assert h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, "exact", False, sol=True) == 0
