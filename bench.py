@@ -134,8 +134,10 @@ def cpu_baseline(w, store, seconds: float):
                       f"{w.seq} keys, in blocks of {block} rows, {el:.1f} s"}
 
 
-def sparse_leg(h3a, dev, reps: int):
-    """kvi8r attention over the 64Q x 64KV tile-masked sparse64k workload (30 % video KV density)."""
+def sparse_legs(h3a, dev, reps: int):
+    """kvi8r attention over the 64Q x 64KV tile-masked sparse64k workload (30 % video KV density):
+    the hard arm (dropped tiles left out) and the Sol arm (each dropped tile one pseudo-key)."""
+    import numpy as np
     import torch
 
     import synth
@@ -149,25 +151,38 @@ def sparse_leg(h3a, dev, reps: int):
         h3a.h3a_kv_quantize(x["k"][t0:t0 + w.q_chunk], kc, sc[0], token_offset=t0)
         h3a.h3a_kv_quantize(x["v"][t0:t0 + w.q_chunk], vc, sc[1], token_offset=t0)
     out = torch.empty_like(x["q"])
-    ws = torch.empty(max(h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, w.q_chunk, "kvi8r", True), 256),
-                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    call = lambda: h3a.h3a_attention(x["q"], kc, vc, sc, out, q_chunk=w.q_chunk, mode="kvi8r", tile_mask=mask,
-                                     workspace=ws)
-    call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(reps):
+    # query rows per q-tile and pseudo-keys (dropped tiles) per (head, q-tile)
+    rows = np.full(w.n_tiles, 64.0)
+    rows[-1] = w.seq - 64 * (w.n_tiles - 1)
+    pseudo_flops = float(4.0 * 128 * np.einsum("hq,q->", (mask_np == 0).sum(axis=2).astype(np.float64), rows))
+    res = {}
+    for sol in (False, True):
+        ws = torch.empty(max(h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, w.q_chunk, "kvi8r", True,
+                                                               sol=sol), 256), dtype=torch.uint8, device=dev)
+        call = lambda: h3a.h3a_attention(x["q"], kc, vc, sc, out, q_chunk=w.q_chunk, mode="kvi8r", tile_mask=mask,
+                                         sol=sol, workspace=ws)
         call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    flops = attention_flops(w, mask_np)
-    tflops = flops / (ms / 1000) / 1e12
-    return {"workload": w.name, "mode": "kvi8r", "seq": w.seq, "heads": w.heads, "q_chunk": w.q_chunk,
-            "kept_tile_frac": round(float(mask_np.mean()), 4), "tflop_algorithmic": round(flops / 1e12, 3),
-            "ms": round(ms, 3), "tflops": round(tflops, 2), "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4)}
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = attention_flops(w, mask_np) + (pseudo_flops if sol else 0.0)
+        tflops = flops / (ms / 1000) / 1e12
+        r = {"workload": w.name, "mode": "kvi8r", "arm": "sol" if sol else "hard", "seq": w.seq, "heads": w.heads,
+             "q_chunk": w.q_chunk, "kept_tile_frac": round(float(mask_np.mean()), 4),
+             "tflop_algorithmic": round(flops / 1e12, 3), "ms": round(ms, 3), "tflops": round(tflops, 2),
+             "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4)}
+        if sol:
+            r["pseudo_keys_per_row"] = round(float((mask_np == 0).sum(axis=2).mean()), 1)
+            r["ms_over_hard"] = round(ms - res["sparse64k"]["ms"], 3)
+        res["sparse64k_sol" if sol else "sparse64k"] = r
+        del ws
+    return res
 
 
 def main() -> int:
@@ -178,10 +193,12 @@ def main() -> int:
     ap.add_argument("--workload", default="long217k")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse (sparse64k) leg")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the block-sparse (sparse64k) legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run one plain 1 GiB device-to-device copy (a known-size "
                          "reference for HBM traffic counters)")
+    ap.add_argument("--sparse-only", action="store_true",
+                    help="run only the block-sparse legs and print their JSON (for profiling the sparse kernels)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -199,6 +216,9 @@ def main() -> int:
         raise SystemExit("bench.py times the dense long-sequence workload; sparse workloads are parity cases")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sparse_only:
+        print(json.dumps(sparse_legs(h3a, dev, reps=max(args.steps, 1))), flush=True)
+        return 0
     log(f"generating {w.name}: S={w.seq} H={w.heads}")
     t_gen = time.time()
     x = make_inputs(w)
@@ -310,8 +330,8 @@ def main() -> int:
         log("sparse64k leg ...")
         del x, out_r, out_e, ws
         torch.cuda.empty_cache()
-        res["sparse64k"] = sparse_leg(h3a, dev, reps=3)
-        log(f"sparse64k: {res['sparse64k']['tflops']} TFLOP/s")
+        res.update(sparse_legs(h3a, dev, reps=3))
+        log(f"sparse64k: hard {res['sparse64k']['tflops']} TFLOP/s, sol {res['sparse64k_sol']['tflops']} TFLOP/s")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(w, (kc, vc, sc), args.cpu_seconds)
