@@ -20,11 +20,14 @@ fp64 NumPy throughout, per-head processing.  What it follows:
 * "H3-Optimizations" page, Nodes (H3 Sparse Attention and the routed-geometry
   paragraph): 64Q x 64KV tiles, the hard arm drops rejected tiles, the Sol arm
   stands in for them with block-mean K and block-sum V.
+* Node page, Inputs table, exact_av_rows row: chosen query rows attend a bf16
+  K/V exactly while the rest use the quantised store.
 
 Modules: ``hadamard`` (the basis), ``encodings`` (exact bf16/fp16 decoding and
 fp16 rounding), ``kvi8r`` (quantise / dequantise), ``attention`` (exact, kvi8r,
 tile-masked and blockwise log-sum-exp attention), ``sol`` (tile-masked
-attention with the dropped tiles' block-mean residual).
+attention with the dropped tiles' block-mean residual), ``routing`` (per-row
+choice between the exact and the kvi8r store).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, brute force and an independent library
@@ -36,11 +39,12 @@ from .kvi8r import rotate_rows, row_scales, codes_for_scales, quantize_rows, deq
 from .attention import (attention, attention_blockwise, kvi8r_attention, expand_tile_mask,
                         exact_attention_bf16)
 from .sol import tile_summaries, sol_attention, exact_sol_attention_bf16, kvi8r_sol_attention
+from .routing import spans_to_rows, routed_attention
 
 __all__ = [
     "sylvester_hadamard", "orthonormal_hadamard", "bf16_to_f64", "f16_to_f64", "f64_to_f16_bits",
     "rotate_rows", "row_scales", "codes_for_scales", "quantize_rows", "dequantize_rows",
     "attention", "attention_blockwise", "kvi8r_attention", "expand_tile_mask",
     "tile_summaries", "sol_attention", "exact_sol_attention_bf16", "kvi8r_sol_attention",
-    "exact_attention_bf16",
+    "exact_attention_bf16", "spans_to_rows", "routed_attention",
 ]
