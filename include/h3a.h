@@ -153,6 +153,32 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
                       void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * h3a_attention_routed -- h3a_attention over two stores of the same K/V, chosen
+ * per query row [P1 Inputs table, exact_av_rows row: text and audio rows attend
+ * a retained bf16 K/V exactly, the other rows the quantised store].
+ *
+ * Rows inside one of the n_spans [begin, end) spans of exact_spans get exact
+ * attention over k_bf16 / v_bf16 (bf16 [s_kv, n_heads, 128], as
+ * H3A_MODE_EXACT_BF16); every other row gets kvi8r attention over k_codes /
+ * v_codes / scales (as H3A_MODE_KVI8R).  Each row's output is bitwise the one
+ * h3a_attention gives it in that mode.  Rows are attended in increasing
+ * order, each stretch of one mode in passes of at most q_chunk rows.
+ *
+ * exact_spans: HOST memory, n_spans pairs of int64 (begin, end) with
+ *              0 <= begin <= end <= s_q, increasing and disjoint
+ *              (end_i <= begin_{i+1}); NULL when n_spans == 0.  Read during
+ *              the call only.
+ * workspace:   h3a_attention_workspace_bytes(s_q, s_kv, n_heads, 128, q_chunk,
+ *              H3A_MODE_KVI8R, 0) bytes.
+ * Other arguments as for h3a_attention.  Dense only (no tile_mask).
+ */
+int32_t h3a_attention_routed(const void* q, const void* k_bf16, const void* v_bf16, const void* k_codes,
+                             const void* v_codes, const void* scales, int64_t s_q, int64_t s_kv, int32_t n_heads,
+                             int32_t head_dim, float softmax_scale, int64_t q_chunk, int64_t kv_block,
+                             const int64_t* exact_spans, int32_t n_spans, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/*
  * h3a_rotate_rows -- y = fp16(x H) for n_rows rows of 128 bf16 values (the
  * query rotation of the kvi8r mode [P1 kv_store]; the same kernel that
  * h3a_attention runs).  x bf16 [n_rows, 128], y fp16 [n_rows, 128], both

@@ -7,7 +7,7 @@ pass their device pointers, shapes and the current HIP stream to the library.
 There is no CPU fallback: if the library is not built, or its ABI version does
 not match, every call raises.
 
-Functions carry the C names: h3a_kv_quantize, h3a_attention,
+Functions carry the C names: h3a_kv_quantize, h3a_attention, h3a_attention_routed,
 h3a_attention_workspace_bytes, h3a_rotate_rows, h3a_unrotate_rows,
 h3a_timing_enable, h3a_timing_collect, h3a_abi_version.
 """
@@ -61,6 +61,9 @@ def _load():
     lib.h3a_attention_workspace_bytes.argtypes = [i64, i64, i32, i32, i64, i32, i32]
     lib.h3a_attention.restype = i32
     lib.h3a_attention.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64, i32, vp, vp, vp, sz, vp]
+    lib.h3a_attention_routed.restype = i32
+    lib.h3a_attention_routed.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64,
+                                         ctypes.POINTER(ctypes.c_int64), i32, vp, vp, sz, vp]
     lib.h3a_rotate_rows.restype = i32
     lib.h3a_rotate_rows.argtypes = [vp, vp, i64, vp]
     lib.h3a_unrotate_rows.restype = i32
@@ -182,6 +185,46 @@ def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: i
     _check(lib.h3a_attention(_ptr(q), _ptr(k_store), _ptr(v_store), _ptr(scales), s_q, s_kv, n_heads, head_dim,
                              float(softmax_scale), int(q_chunk), int(kv_block), int(mode) | flags, _ptr(tile_mask),
                              _ptr(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def h3a_attention_routed(q, k_bf16, v_bf16, store, out, *, exact_spans, q_chunk: int, kv_block: int = 0,
+                         softmax_scale: float | None = None, workspace=None, stream=None):
+    """Attention of q (bf16 [s_q, H, 128]) into out, rows chosen per span between two stores of one K/V.
+
+    Rows inside one of exact_spans (increasing, disjoint [begin, end) pairs) attend k_bf16 / v_bf16
+    (bf16 [s_kv, H, 128]) exactly; the other rows attend the kvi8r store = (k_codes, v_codes, scales).
+    """
+    lib = _load()
+    kc, vc, sc = store
+    _need(q, "q", torch.bfloat16)
+    _need(out, "out", torch.bfloat16)
+    _need(k_bf16, "k_bf16", torch.bfloat16)
+    _need(v_bf16, "v_bf16", torch.bfloat16)
+    _need(kc, "k_codes", torch.int8)
+    _need(vc, "v_codes", torch.int8)
+    _need(sc, "scales", torch.float16)
+    for name, t in (("q", q), ("out", out), ("k_bf16", k_bf16), ("v_bf16", v_bf16), ("k_codes", kc),
+                    ("v_codes", vc), ("scales", sc)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be [s_q, n_heads, head_dim] tensors of equal shape")
+    s_q, n_heads, head_dim = q.shape
+    s_kv = k_bf16.shape[0]
+    if kc.shape[1] != s_kv:
+        raise ValueError("the bf16 K/V and the kvi8r store must hold the same number of tokens")
+    flat = [int(x) for span in exact_spans for x in span]
+    spans = (ctypes.c_int64 * max(len(flat), 1))(*flat)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    need = int(lib.h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, MODE_KVI8R, 0))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.h3a_attention_routed(_ptr(q), _ptr(k_bf16), _ptr(v_bf16), _ptr(kc), _ptr(vc), _ptr(sc), s_q, s_kv,
+                                    n_heads, head_dim, float(softmax_scale), int(q_chunk), int(kv_block), spans,
+                                    len(flat) // 2, _ptr(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
     return out
 
 

@@ -126,6 +126,167 @@ std::mutex g_timing_mu;
 bool g_timing_on = false;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
 
+// ---- argument checks shared by the attention entry points ----------------------
+int check_shapes(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chunk, int64_t kv_block,
+                 float softmax_scale) {
+  if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
+  if (s_q < 0 || s_kv < 0) return fail(H3A_EINVAL, "s_q and s_kv must be >= 0");
+  if (s_q > ((int64_t)1 << 31) || s_kv > ((int64_t)1 << 31)) return fail(H3A_EINVAL, "sequence too long");
+  if (q_chunk < 1) return fail(H3A_EINVAL, "q_chunk must be >= 1 (got %lld)", (long long)q_chunk);
+  if (kv_block < 0 || kv_block % H3A_TILE != 0)
+    return fail(H3A_EINVAL, "kv_block must be 0 or a positive multiple of 64 (got %lld)", (long long)kv_block);
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
+    return fail(H3A_EINVAL, "softmax_scale must be finite and > 0");
+  return H3A_OK;
+}
+
+// q and out: bf16 [s_q, n_heads, 128].
+int check_rows(const void* q, const void* out, int64_t s_q, int32_t n_heads) {
+  int64_t n;
+  if (!mul_ok(s_q, (int64_t)n_heads * H3A_HEAD_DIM, &n)) return fail(H3A_EINVAL, "size overflow");
+  int rc;
+  if ((rc = check_buffer(q, (uint64_t)n * 2, 16, "q")) != H3A_OK) return rc;
+  return check_buffer(out, (uint64_t)n * 2, 16, "out");
+}
+
+// One K/V store of `mode` over s_kv tokens.
+int check_store(int32_t mode, const void* k, const void* v, const void* scales, int64_t s_kv, int32_t n_heads,
+                const char* k_name, const char* v_name) {
+  int64_t n;
+  if (!mul_ok(s_kv, (int64_t)n_heads * H3A_HEAD_DIM, &n)) return fail(H3A_EINVAL, "size overflow");
+  const bool q8 = mode == H3A_MODE_KVI8R;
+  const uint64_t bytes = (uint64_t)n * (q8 ? 1 : 2);
+  int rc;
+  if ((rc = check_buffer(k, bytes, 16, k_name)) != H3A_OK) return rc;
+  if ((rc = check_buffer(v, bytes, 16, v_name)) != H3A_OK) return rc;
+  if (q8) return check_buffer(scales, (uint64_t)s_kv * n_heads * 4, 2, "scales");
+  return H3A_OK;
+}
+
+int check_workspace(const void* workspace, size_t workspace_bytes, const WorkspaceLayout& wl) {
+  if (wl.total == 0) return H3A_OK;
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(H3A_EWORKSPACE, "workspace needs %llu bytes (got %llu)", (unsigned long long)wl.total,
+                (unsigned long long)(workspace == nullptr ? 0 : workspace_bytes));
+  return check_buffer(workspace, wl.total, 256, "workspace");
+}
+
+// ---- the query-chunk loop -----------------------------------------------------------
+// One validated call over one store.
+struct Pass {
+  int32_t mode = 0;
+  bool sol = false;
+  const uint16_t* q = nullptr;
+  uint16_t* out = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const uint16_t* k_scale = nullptr;
+  const uint16_t* v_scale = nullptr;
+  int64_t s_q = 0, s_kv = 0;
+  int32_t n_heads = 0;
+  float scale_log2 = 0.0f;
+  int64_t q_chunk = 0;
+  const uint8_t* tile_mask = nullptr;  // sparse when set; passes then start at multiples of 64 rows
+  char* ws = nullptr;
+  WorkspaceLayout wl;
+  hipStream_t st = nullptr;
+  bool timing = false;
+};
+
+Pass make_pass(int32_t mode, const void* q, void* out, const void* k, const void* v, const void* scales,
+               int64_t s_q, int64_t s_kv, int32_t n_heads, float softmax_scale, int64_t q_chunk, char* ws,
+               const WorkspaceLayout& wl, void* stream) {
+  Pass p;
+  p.mode = mode;
+  p.q = static_cast<const uint16_t*>(q);
+  p.out = static_cast<uint16_t*>(out);
+  p.k = k;
+  p.v = v;
+  if (mode == H3A_MODE_KVI8R) {
+    p.k_scale = static_cast<const uint16_t*>(scales);
+    p.v_scale = p.k_scale + s_kv * n_heads;
+  }
+  p.s_q = s_q;
+  p.s_kv = s_kv;
+  p.n_heads = n_heads;
+  p.scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.q_chunk = q_chunk;
+  p.ws = ws;
+  p.wl = wl;
+  p.st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  p.timing = g_timing_on;
+  return p;
+}
+
+// Query rows [r0, r1), in passes of at most q_chunk rows ("H3 Streamed Blocks"
+// node page, "How it works": each query chunk attends the whole K/V store).
+int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
+  const int64_t n_qt_total = (p.s_q + H3A_TILE - 1) / H3A_TILE, n_kt = (p.s_kv + H3A_TILE - 1) / H3A_TILE;
+  const bool sparse = p.tile_mask != nullptr;
+  for (int64_t c0 = r0; c0 < r1; c0 += p.q_chunk) {
+    const int64_t rows = (r1 - c0) < p.q_chunk ? (r1 - c0) : p.q_chunk;
+    const int64_t off = c0 * p.n_heads * H3A_HEAD_DIM;
+    h3a::AttnChunk a{};
+    h3a::SolArgs sa{};
+    a.rows = rows;
+    a.s_kv = p.s_kv;
+    a.n_heads = p.n_heads;
+    a.scale_log2 = p.scale_log2;
+    a.k = p.k;
+    a.v = p.v;
+    hipError_t e;
+    if (p.mode == H3A_MODE_KVI8R) {
+      uint16_t* qrot = reinterpret_cast<uint16_t*>(p.ws + p.wl.qrot);
+      if ((e = h3a::launch_rotate_q(p.q + off, qrot, rows * p.n_heads, p.st)) != hipSuccess)
+        return hip_fail(e, "rotate_q launch");
+      a.q = qrot;
+      a.k_scale = p.k_scale;
+      a.v_scale = p.v_scale;
+      a.out = p.ws + p.wl.orot;
+    } else {
+      a.q = p.q + off;
+      a.out = p.out + off;
+    }
+    if (sparse) {
+      a.counts = reinterpret_cast<const int32_t*>(p.ws + p.wl.counts);
+      a.lists = reinterpret_cast<const int32_t*>(p.ws + p.wl.lists);
+      int32_t* drops = nullptr;
+      if (p.sol) {
+        drops = reinterpret_cast<int32_t*>(p.ws + p.wl.drops);
+        sa.drops = drops;
+        sa.kmean = reinterpret_cast<const uint16_t*>(p.ws + p.wl.kmean);
+        sa.vmean = reinterpret_cast<const uint16_t*>(p.ws + p.wl.vmean);
+        sa.kmscale = reinterpret_cast<const float*>(p.ws + p.wl.kmscale);
+      }
+      const int32_t n_qt = (int32_t)((rows + H3A_TILE - 1) / H3A_TILE);
+      if ((e = h3a::launch_route_build(p.tile_mask, n_qt_total, c0 / H3A_TILE, n_qt, (int32_t)n_kt, p.n_heads,
+                                       reinterpret_cast<int32_t*>(p.ws + p.wl.counts),
+                                       reinterpret_cast<int32_t*>(p.ws + p.wl.lists), drops, p.st)) != hipSuccess)
+        return hip_fail(e, "route_build launch");
+    }
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    if (p.timing) {
+      if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess)
+        return hip_fail(e, "hipEventCreate");
+      if ((e = hipEventRecord(ev0, p.st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    if ((e = h3a::launch_attn_fwd(p.mode, sparse, a, p.sol ? &sa : nullptr, p.st)) != hipSuccess)
+      return hip_fail(e, "attn_fwd launch");
+    if (p.timing) {
+      if ((e = hipEventRecord(ev1, p.st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      std::lock_guard<std::mutex> lk(g_timing_mu);
+      g_events.emplace_back(ev0, ev1);
+    }
+    if (p.mode == H3A_MODE_KVI8R) {
+      if ((e = h3a::launch_unrotate_o(reinterpret_cast<const float*>(p.ws + p.wl.orot), p.out + off,
+                                      rows * p.n_heads, p.st)) != hipSuccess)
+        return hip_fail(e, "unrotate_o launch");
+    }
+  }
+  return H3A_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -187,14 +348,8 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
   if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R) return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
   if (sol && tile_mask == nullptr) return fail(H3A_EINVAL, "H3A_SOL needs a tile_mask");
   if (sol && s_kv > h3a::kSolMaxKv) return fail(H3A_EINVAL, "H3A_SOL supports s_kv up to 2^30 - 64");
-  if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
-  if (s_q < 0 || s_kv < 0) return fail(H3A_EINVAL, "s_q and s_kv must be >= 0");
-  if (s_q > ((int64_t)1 << 31) || s_kv > ((int64_t)1 << 31)) return fail(H3A_EINVAL, "sequence too long");
-  if (q_chunk < 1) return fail(H3A_EINVAL, "q_chunk must be >= 1 (got %lld)", (long long)q_chunk);
-  if (kv_block < 0 || kv_block % H3A_TILE != 0)
-    return fail(H3A_EINVAL, "kv_block must be 0 or a positive multiple of 64 (got %lld)", (long long)kv_block);
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale))
-    return fail(H3A_EINVAL, "softmax_scale must be finite and > 0");
+  int rc;
+  if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
   const bool sparse = tile_mask != nullptr;
   if (sparse && q_chunk % H3A_TILE != 0)
     return fail(H3A_EINVAL, "q_chunk must be a multiple of 64 with a tile_mask (got %lld)", (long long)q_chunk);
@@ -203,18 +358,9 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
   if (mode == H3A_MODE_EXACT_BF16 && scales != nullptr) return fail(H3A_EINVAL, "exact mode takes no scales");
   if (s_q == 0) return H3A_OK;
 
-  int64_t n_qkv, n_kv;
-  if (!mul_ok(s_q, (int64_t)n_heads * H3A_HEAD_DIM, &n_qkv) || !mul_ok(s_kv, (int64_t)n_heads * H3A_HEAD_DIM, &n_kv))
-    return fail(H3A_EINVAL, "size overflow");
+  if ((rc = check_rows(q, out, s_q, n_heads)) != H3A_OK) return rc;
+  if ((rc = check_store(mode, k_store, v_store, scales, s_kv, n_heads, "k_store", "v_store")) != H3A_OK) return rc;
   const int64_t n_qt_total = (s_q + H3A_TILE - 1) / H3A_TILE, n_kt = (s_kv + H3A_TILE - 1) / H3A_TILE;
-  int rc;
-  if ((rc = check_buffer(q, (uint64_t)n_qkv * 2, 16, "q")) != H3A_OK) return rc;
-  if ((rc = check_buffer(out, (uint64_t)n_qkv * 2, 16, "out")) != H3A_OK) return rc;
-  const uint64_t kv_bytes = (uint64_t)n_kv * (mode == H3A_MODE_KVI8R ? 1 : 2);
-  if ((rc = check_buffer(k_store, kv_bytes, 16, "k_store")) != H3A_OK) return rc;
-  if ((rc = check_buffer(v_store, kv_bytes, 16, "v_store")) != H3A_OK) return rc;
-  if (mode == H3A_MODE_KVI8R && (rc = check_buffer(scales, (uint64_t)s_kv * n_heads * 4, 2, "scales")) != H3A_OK)
-    return rc;
   if (sparse) {
     int64_t mb;
     if (!mul_ok(n_qt_total * n_heads, n_kt, &mb)) return fail(H3A_EINVAL, "tile_mask size overflow");
@@ -223,92 +369,65 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
   WorkspaceLayout wl;
   if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse, sol, &wl))
     return fail(H3A_EINVAL, "size overflow");
-  if (wl.total > 0) {
-    if (workspace == nullptr || workspace_bytes < wl.total)
-      return fail(H3A_EWORKSPACE, "workspace needs %llu bytes (got %llu)", (unsigned long long)wl.total,
-                  (unsigned long long)(workspace == nullptr ? 0 : workspace_bytes));
-    if ((rc = check_buffer(workspace, wl.total, 256, "workspace")) != H3A_OK) return rc;
-  }
+  if ((rc = check_workspace(workspace, workspace_bytes, wl)) != H3A_OK) return rc;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  const uint16_t* qb = static_cast<const uint16_t*>(q);
-  uint16_t* ob = static_cast<uint16_t*>(out);
-  bool timing;
-  {
-    std::lock_guard<std::mutex> lk(g_timing_mu);
-    timing = g_timing_on;
-  }
-  const uint16_t* kv_scales = static_cast<const uint16_t*>(scales);
-  const uint16_t* k_scale = mode == H3A_MODE_KVI8R ? kv_scales : nullptr;
-  const uint16_t* v_scale = mode == H3A_MODE_KVI8R ? kv_scales + s_kv * n_heads : nullptr;
+  Pass p = make_pass(mode, q, out, k_store, v_store, scales, s_q, s_kv, n_heads, softmax_scale, q_chunk,
+                     static_cast<char*>(workspace), wl, stream);
+  p.tile_mask = tile_mask;
+  p.sol = sol;
   if (sol) {
-    hipError_t e = h3a::launch_tile_means(mode, k_store, v_store, k_scale, v_scale, s_kv, n_heads,
-                                          reinterpret_cast<uint16_t*>(ws + wl.kmean),
-                                          reinterpret_cast<uint16_t*>(ws + wl.vmean),
-                                          reinterpret_cast<float*>(ws + wl.kmscale), st);
+    hipError_t e = h3a::launch_tile_means(mode, k_store, v_store, p.k_scale, p.v_scale, s_kv, n_heads,
+                                          reinterpret_cast<uint16_t*>(p.ws + wl.kmean),
+                                          reinterpret_cast<uint16_t*>(p.ws + wl.vmean),
+                                          reinterpret_cast<float*>(p.ws + wl.kmscale), p.st);
     if (e != hipSuccess) return hip_fail(e, "tile_means launch");
   }
-  for (int64_t c0 = 0; c0 < s_q; c0 += q_chunk) {
-    const int64_t rows = (s_q - c0) < q_chunk ? (s_q - c0) : q_chunk;
-    const int64_t off = c0 * n_heads * H3A_HEAD_DIM;
-    h3a::AttnChunk a{};
-    h3a::SolArgs sa{};
-    a.rows = rows;
-    a.s_kv = s_kv;
-    a.n_heads = n_heads;
-    a.scale_log2 = scale_log2;
-    a.k = k_store;
-    a.v = v_store;
-    hipError_t e;
-    if (mode == H3A_MODE_KVI8R) {
-      uint16_t* qrot = reinterpret_cast<uint16_t*>(ws + wl.qrot);
-      if ((e = h3a::launch_rotate_q(qb + off, qrot, rows * n_heads, st)) != hipSuccess)
-        return hip_fail(e, "rotate_q launch");
-      a.q = qrot;
-      a.k_scale = k_scale;
-      a.v_scale = v_scale;
-      a.out = ws + wl.orot;
-    } else {
-      a.q = qb + off;
-      a.out = ob + off;
-    }
-    if (sparse) {
-      a.counts = reinterpret_cast<const int32_t*>(ws + wl.counts);
-      a.lists = reinterpret_cast<const int32_t*>(ws + wl.lists);
-      int32_t* drops = nullptr;
-      if (sol) {
-        drops = reinterpret_cast<int32_t*>(ws + wl.drops);
-        sa.drops = drops;
-        sa.kmean = reinterpret_cast<const uint16_t*>(ws + wl.kmean);
-        sa.vmean = reinterpret_cast<const uint16_t*>(ws + wl.vmean);
-        sa.kmscale = reinterpret_cast<const float*>(ws + wl.kmscale);
-      }
-      const int32_t n_qt = (int32_t)((rows + H3A_TILE - 1) / H3A_TILE);
-      if ((e = h3a::launch_route_build(tile_mask, n_qt_total, c0 / H3A_TILE, n_qt, (int32_t)n_kt, n_heads,
-                                       reinterpret_cast<int32_t*>(ws + wl.counts),
-                                       reinterpret_cast<int32_t*>(ws + wl.lists), drops, st)) != hipSuccess)
-        return hip_fail(e, "route_build launch");
-    }
-    hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    if (timing) {
-      if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess)
-        return hip_fail(e, "hipEventCreate");
-      if ((e = hipEventRecord(ev0, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
-    if ((e = h3a::launch_attn_fwd(mode, sparse, a, sol ? &sa : nullptr, st)) != hipSuccess)
-      return hip_fail(e, "attn_fwd launch");
-    if (timing) {
-      if ((e = hipEventRecord(ev1, st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-      std::lock_guard<std::mutex> lk(g_timing_mu);
-      g_events.emplace_back(ev0, ev1);
-    }
-    if (mode == H3A_MODE_KVI8R) {
-      if ((e = h3a::launch_unrotate_o(reinterpret_cast<const float*>(ws + wl.orot), ob + off, rows * n_heads, st)) !=
-          hipSuccess)
-        return hip_fail(e, "unrotate_o launch");
-    }
+  return attend_rows(p, 0, s_q);
+}
+
+int32_t h3a_attention_routed(const void* q, const void* k_bf16, const void* v_bf16, const void* k_codes,
+                             const void* v_codes, const void* scales, int64_t s_q, int64_t s_kv, int32_t n_heads,
+                             int32_t head_dim, float softmax_scale, int64_t q_chunk, int64_t kv_block,
+                             const int64_t* exact_spans, int32_t n_spans, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  int rc;
+  if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
+  if (n_spans < 0 || (n_spans > 0 && exact_spans == nullptr))
+    return fail(H3A_EINVAL, "exact_spans must hold n_spans >= 0 [begin, end) pairs");
+  int64_t prev_end = 0;
+  for (int32_t i = 0; i < n_spans; ++i) {
+    const int64_t b = exact_spans[2 * i], e = exact_spans[2 * i + 1];
+    if (!(prev_end <= b && b <= e && e <= s_q))
+      return fail(H3A_EINVAL, "exact span %d [%lld, %lld) is out of order or outside [0, s_q = %lld]", i,
+                  (long long)b, (long long)e, (long long)s_q);
+    prev_end = e;
+  }
+  if (scales == nullptr && s_kv > 0) return fail(H3A_EINVAL, "the kvi8r store needs scales");
+  if (s_q == 0) return H3A_OK;
+  if ((rc = check_rows(q, out, s_q, n_heads)) != H3A_OK) return rc;
+  if ((rc = check_store(H3A_MODE_EXACT_BF16, k_bf16, v_bf16, nullptr, s_kv, n_heads, "k_bf16", "v_bf16")) != H3A_OK)
+    return rc;
+  if ((rc = check_store(H3A_MODE_KVI8R, k_codes, v_codes, scales, s_kv, n_heads, "k_codes", "v_codes")) != H3A_OK)
+    return rc;
+  WorkspaceLayout wl;
+  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, H3A_MODE_KVI8R, false, false, &wl))
+    return fail(H3A_EINVAL, "size overflow");
+  if ((rc = check_workspace(workspace, workspace_bytes, wl)) != H3A_OK) return rc;
+
+  char* ws = static_cast<char*>(workspace);
+  const Pass exact = make_pass(H3A_MODE_EXACT_BF16, q, out, k_bf16, v_bf16, nullptr, s_q, s_kv, n_heads,
+                               softmax_scale, q_chunk, ws, wl, stream);
+  const Pass quant = make_pass(H3A_MODE_KVI8R, q, out, k_codes, v_codes, scales, s_q, s_kv, n_heads,
+                               softmax_scale, q_chunk, ws, wl, stream);
+  // Rows in increasing order: the kvi8r stretch before each span, then the span.
+  int64_t r = 0;
+  for (int32_t i = 0; i <= n_spans; ++i) {
+    const int64_t b = i < n_spans ? exact_spans[2 * i] : s_q, e = i < n_spans ? exact_spans[2 * i + 1] : s_q;
+    if ((rc = attend_rows(quant, r, b)) != H3A_OK) return rc;
+    if ((rc = attend_rows(exact, b, e)) != H3A_OK) return rc;
+    r = e;
   }
   return H3A_OK;
 }

@@ -28,8 +28,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for need in ("h3a_kv_quantize", "h3a_attention", "h3a_attention_workspace_bytes", "h3a_abi_version",
-                 "h3a_last_error", "h3a_rotate_rows", "h3a_unrotate_rows"):
+    for need in ("h3a_kv_quantize", "h3a_attention", "h3a_attention_routed", "h3a_attention_workspace_bytes",
+                 "h3a_abi_version", "h3a_last_error", "h3a_rotate_rows", "h3a_unrotate_rows"):
         assert need in names
 
 
@@ -76,6 +76,39 @@ def test_attention_rejects_bad_arguments(lib, kw, status, msg):
 
 def test_attention_empty_query_is_noop(lib):
     assert _attn(lib, s_q=0, scales=16) == 0
+
+
+def _routed(lib, spans, **kw):
+    import ctypes
+
+    a = dict(s_q=1024, s_kv=1024, n_heads=2, head_dim=128, scale=0.088, q_chunk=256, kv_block=0, scales=16)
+    a.update(kw)
+    flat = [x for sp in (spans or []) for x in sp]
+    arr = (ctypes.c_int64 * max(len(flat), 1))(*flat) if spans is not None else None
+    n = kw.get("n_spans", len(flat) // 2)
+    return lib.h3a_attention_routed(None, None, None, None, None, a["scales"], a["s_q"], a["s_kv"], a["n_heads"],
+                                    a["head_dim"], a["scale"], a["q_chunk"], a["kv_block"], arr, n, None, None, 0,
+                                    None)
+
+
+@pytest.mark.parametrize("spans,kw,status,msg", [
+    ([(0, 64)], dict(head_dim=64), -2, "head_dim"),
+    ([(10, 5)], {}, -1, "exact span 0"),
+    ([(0, 100), (50, 200)], {}, -1, "exact span 1"),
+    ([(0, 100), (900, 1025)], {}, -1, "exact span 1"),
+    ([(-1, 10)], {}, -1, "exact span 0"),
+    (None, dict(n_spans=2), -1, "exact_spans"),
+    ([(0, 10)], dict(n_spans=-1), -1, "exact_spans"),
+    ([(0, 64)], dict(scales=None), -1, "scales"),
+    ([(0, 64)], dict(q_chunk=0), -1, "q_chunk"),
+])
+def test_routed_rejects_bad_arguments(lib, spans, kw, status, msg):
+    assert _routed(lib, spans, **kw) == status
+    assert msg in lib.h3a_last_error().decode()
+
+
+def test_routed_empty_query_is_noop(lib):
+    assert _routed(lib, [(0, 0)], s_q=0) == 0
 
 
 @pytest.mark.parametrize("kw,status,msg", [
