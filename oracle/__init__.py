@@ -16,7 +16,8 @@ fp64 NumPy throughout, per-head processing.  What it follows:
   online-softmax combine.  Same row: q_chunk "exact at any value".
 * "Low VRAM, low RAM: the de-rope on a 16 GB card" page, "The K/V store
   options": scores are invariant under the rotation, P.V is brought back
-  through the transpose once; fp16 rather than bf16 inside kvi8r.
+  through the transpose once; fp16 rather than bf16 inside kvi8r.  "What is
+  next": a kvi8r variant with one scale per 32 values.
 * "H3-Optimizations" page, Nodes (H3 Sparse Attention and the routed-geometry
   paragraph): 64Q x 64KV tiles, the hard arm drops rejected tiles, the Sol arm
   stands in for them with block-mean K and block-sum V.
@@ -35,7 +36,8 @@ routine; none is "parity unpinned".
 """
 from .hadamard import sylvester_hadamard, orthonormal_hadamard
 from .encodings import bf16_to_f64, f16_to_f64, f64_to_f16_bits
-from .kvi8r import rotate_rows, row_scales, codes_for_scales, quantize_rows, dequantize_rows
+from .kvi8r import (rotate_rows, row_scales, codes_for_scales, quantize_rows, dequantize_rows,
+                    quantize_rows_grouped, dequantize_rows_grouped)
 from .attention import (attention, attention_blockwise, kvi8r_attention, expand_tile_mask,
                         exact_attention_bf16)
 from .sol import tile_summaries, sol_attention, exact_sol_attention_bf16, kvi8r_sol_attention
@@ -44,6 +46,7 @@ from .routing import spans_to_rows, routed_attention
 __all__ = [
     "sylvester_hadamard", "orthonormal_hadamard", "bf16_to_f64", "f16_to_f64", "f64_to_f16_bits",
     "rotate_rows", "row_scales", "codes_for_scales", "quantize_rows", "dequantize_rows",
+    "quantize_rows_grouped", "dequantize_rows_grouped",
     "attention", "attention_blockwise", "kvi8r_attention", "expand_tile_mask",
     "tile_summaries", "sol_attention", "exact_sol_attention_bf16", "kvi8r_sol_attention",
     "exact_attention_bf16", "spans_to_rows", "routed_attention",

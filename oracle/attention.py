@@ -19,7 +19,7 @@ import numpy as np
 
 from .encodings import bf16_to_f64
 from .hadamard import orthonormal_hadamard
-from .kvi8r import dequantize_rows
+from .kvi8r import dequantize_rows, dequantize_rows_grouped
 
 TILE = 64
 
@@ -103,11 +103,17 @@ def kvi8r_attention(q, k_codes, k_scale_bits, v_codes, v_scale_bits, scale: floa
     """kvi8r attention of one head.
 
     q: fp64 [n, 128] in the original basis.  K/V: int8 codes [m, 128] and fp16
-    scale bits [m] in the rotated basis.  q' = q H; O' = softmax(q' K^T s) V with
+    scale bits in the rotated basis, [m] (one per row) or [m, 4] (one per 32
+    values, the per-32-value variant).  q' = q H; O' = softmax(q' K^T s) V with
     K, V the exact dequantised rows; O = O' H^T (= O' H, H symmetric).
     """
     h = orthonormal_hadamard(np.asarray(q).shape[-1])
     q_rot = np.asarray(q, dtype=np.float64) @ h
-    o_rot = attention(q_rot, dequantize_rows(k_codes, k_scale_bits),
-                      dequantize_rows(v_codes, v_scale_bits), scale, keep)
+    o_rot = attention(q_rot, _dequantize(k_codes, k_scale_bits), _dequantize(v_codes, v_scale_bits), scale, keep)
     return o_rot @ h.T
+
+
+def _dequantize(codes, scale_bits):
+    if np.asarray(scale_bits).ndim == 2:
+        return dequantize_rows_grouped(codes, scale_bits)
+    return dequantize_rows(codes, scale_bits)

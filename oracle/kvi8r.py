@@ -17,6 +17,12 @@ Readings where the pages are silent (each is listed in the design notes):
 * the code is an integer decided by floating point, so it is decided in the
   kernel's precision, fp32: q = round-half-even(fp32(y) / fp32(s)) with the
   quotient correctly rounded to fp32.  Every other step is fp64.
+
+Per-32-value variant ("Low VRAM, low RAM" page, "What is next": a kvi8r variant
+with a scale per 32 values, finer than per row).  Reading: each rotated row is
+cut into four groups of 32 consecutive values (rotated dims 0-31, 32-63, 64-95,
+96-127) and every group is quantised exactly as a row is above, with its own
+fp16 scale.
 """
 from __future__ import annotations
 
@@ -26,6 +32,7 @@ from .encodings import f16_to_f64, f64_to_f16_bits
 from .hadamard import orthonormal_hadamard
 
 QMAX = 127
+GROUP = 32  # values per scale in the per-32-value variant
 
 
 def rotate_rows(x: np.ndarray) -> np.ndarray:
@@ -69,3 +76,23 @@ def quantize_rows(x: np.ndarray):
 def dequantize_rows(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
     """Rotated-basis rows codes * scale, exact in fp64."""
     return np.asarray(codes, dtype=np.float64) * f16_to_f64(scale_bits)[:, None]
+
+
+def quantize_rows_grouped(x: np.ndarray, group: int = GROUP):
+    """Per-group variant of quantize_rows: every `group` consecutive rotated values get their own scale.
+
+    Returns (codes int8 [n, 128], scale bits uint16 [n, 128 // group], y fp64 [n, 128]).
+    """
+    y = rotate_rows(x)
+    n, d = y.shape
+    yg = y.reshape(n * (d // group), group)  # one group per row
+    s = row_scales(yg)
+    return codes_for_scales(yg, s).reshape(n, d), s.reshape(n, d // group), y
+
+
+def dequantize_rows_grouped(codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """Rotated-basis rows: each code times the scale of its group, exact in fp64."""
+    codes = np.asarray(codes, dtype=np.float64)
+    n, d = codes.shape
+    g = np.asarray(scale_bits).shape[1]
+    return (codes.reshape(n, g, d // g) * f16_to_f64(scale_bits)[:, :, None]).reshape(n, d)

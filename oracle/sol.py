@@ -23,7 +23,7 @@ import numpy as np
 
 from .encodings import bf16_to_f64
 from .hadamard import orthonormal_hadamard
-from .kvi8r import dequantize_rows
+from .kvi8r import dequantize_rows, dequantize_rows_grouped
 
 TILE = 64
 
@@ -81,9 +81,10 @@ def exact_sol_attention_bf16(q_bits, k_bits, v_bits, scale: float, q_rows, mask_
 
 def kvi8r_sol_attention(q, k_codes, k_scale_bits, v_codes, v_scale_bits, scale: float, q_rows,
                         mask_head) -> np.ndarray:
-    """kvi8r store: tile summaries of the dequantised rotated K/V; q rotated in, O rotated back."""
+    """kvi8r store (scales [m] per row or [m, 4] per 32 values): tile summaries of the dequantised
+    rotated K/V; q rotated in, O rotated back."""
     h = orthonormal_hadamard(np.asarray(q).shape[-1])
     q_rot = np.asarray(q, dtype=np.float64) @ h
-    o_rot = sol_attention(q_rot, dequantize_rows(k_codes, k_scale_bits), dequantize_rows(v_codes, v_scale_bits),
-                          scale, q_rows, mask_head)
+    deq = dequantize_rows_grouped if np.asarray(k_scale_bits).ndim == 2 else dequantize_rows
+    o_rot = sol_attention(q_rot, deq(k_codes, k_scale_bits), deq(v_codes, v_scale_bits), scale, q_rows, mask_head)
     return o_rot @ h.T
