@@ -5,16 +5,17 @@
  * What the calls compute follows three pages:
  *   [P1] "H3 Streamed Blocks (exact low-VRAM, alpha)" node page:
  *        "How it works" and the Inputs table (rows q_chunk, kv_chunk, kv_block,
- *        kv_store).
+ *        kv_store, exact_av_rows).
  *   [P2] "Low VRAM, low RAM: the de-rope on a 16 GB card" page:
- *        "The K/V store options" (table and rotation paragraph) and
- *        "What is exact, and what is not".
+ *        "The K/V store options" (table and rotation paragraph),
+ *        "What is exact, and what is not" and "What is next".
  *   [P3] "H3-Optimizations" extension page: "Nodes" (H3 Sparse Attention,
  *        H3 Sparse Attention (Advanced) and the routed-geometry paragraph).
  *
  * Conventions shared by every call
  *   - Every tensor pointer is device memory owned by the caller, and must stay
- *     valid until the work queued on `stream` has finished.  The library keeps
+ *     valid until the work queued on `stream` has finished (the one host
+ *     array, h3a_attention_routed's exact_spans, is read during the call).  The library keeps
  *     no pointer after a call returns and allocates no device memory; scratch
  *     space comes only through the `workspace` argument.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
@@ -53,6 +54,7 @@ extern "C" {
 /* K/V store kinds, named after the kv_store choices they implement [P1 kv_store]. */
 #define H3A_MODE_EXACT_BF16 0 /* "bf16 (exact)": K/V kept as bf16, stock attention math */
 #define H3A_MODE_KVI8R 1      /* "kvi8r": rotated int8 K/V with one fp16 scale per (token, head) row */
+#define H3A_MODE_KVI8R32 2    /* "kvi8r32": the same with one fp16 scale per 32 rotated values [P2 What is next] */
 
 /* Flag OR-ed into mode (with a tile_mask only): every dropped KV tile still
  * contributes, as one pseudo-key -- its block-mean key with its block-mean value,
@@ -96,6 +98,22 @@ int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens,
                         void* scales_f16, void* stream);
 
 /*
+ * h3a_kv_quantize_g32 -- build one kv_chunk of the kvi8r32 store: the
+ * per-32-value scale variant of kvi8r [P2 "What is next": finer than per row].
+ *
+ * As h3a_kv_quantize, except that each rotated row y is cut into four groups
+ * of 32 consecutive values (y_0..y_31, y_32..y_63, y_64..y_95, y_96..y_127) and
+ * every group g gets its own scale_g = fp16(max|y in g| / 127), its codes taken
+ * against scale_g in the same way.
+ *
+ * scales_f16:      fp16 [n_heads, s_total, 4] (head-major, the four group
+ *                  scales of a row together), 8-byte aligned.
+ */
+int32_t h3a_kv_quantize_g32(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads,
+                            int32_t head_dim, int64_t token_offset, int64_t s_total, int8_t* codes,
+                            void* scales_f16, void* stream);
+
+/*
  * h3a_attention_workspace_bytes -- bytes of workspace h3a_attention needs.
  * sparse != 0 when a tile_mask will be passed; mode as passed to h3a_attention
  * (including H3A_SOL).  Returns 0 when none is needed or the arguments are
@@ -111,7 +129,8 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
  *
  *   O[t, h, :] = sum_j softmax_j(softmax_scale * q[t,h,:] . k[j,h,:]) v[j,h,:]
  *
- * mode is H3A_MODE_EXACT_BF16 or H3A_MODE_KVI8R, optionally OR-ed with H3A_SOL.
+ * mode is H3A_MODE_EXACT_BF16, H3A_MODE_KVI8R or H3A_MODE_KVI8R32, optionally OR-ed
+ * with H3A_SOL.
  * mode H3A_MODE_EXACT_BF16: k_store / v_store are bf16 [s_kv, n_heads, 128]
  *   (token-major), scales must be NULL.  Inputs feed bf16 matrix cores, fp32
  *   accumulation.  The output is bitwise identical for every q_chunk and
@@ -122,6 +141,10 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
  *   (rounded to fp16), attends the K/V rows dequantised on the fly as one
  *   int8 -> fp16 cast times the row scale, with fp16 matrix-core products and
  *   fp32 accumulation, and the output is rotated back once per row.
+ * mode H3A_MODE_KVI8R32: as H3A_MODE_KVI8R over the store written by
+ *   h3a_kv_quantize_g32; scales is fp16 [2, n_heads, s_kv, 4], 8-byte aligned.
+ *   Each K and V row is dequantised group by group (code * group scale,
+ *   rounded to fp16) before the fp16 matrix-core products.
  *
  * q:          bf16 [s_q, n_heads, 128], 16-byte aligned.
  * out:        bf16 [s_q, n_heads, 128], 16-byte aligned; must not alias inputs.

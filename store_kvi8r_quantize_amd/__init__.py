@@ -7,7 +7,8 @@ pass their device pointers, shapes and the current HIP stream to the library.
 There is no CPU fallback: if the library is not built, or its ABI version does
 not match, every call raises.
 
-Functions carry the C names: h3a_kv_quantize, h3a_attention, h3a_attention_routed,
+Functions carry the C names: h3a_kv_quantize (+ h3a_kv_quantize_g32, chosen by the
+scales' shape), h3a_attention, h3a_attention_routed,
 h3a_attention_workspace_bytes, h3a_rotate_rows, h3a_unrotate_rows,
 h3a_timing_enable, h3a_timing_collect, h3a_abi_version.
 """
@@ -24,7 +25,8 @@ HEAD_DIM = 128
 TILE = 64
 MODE_EXACT_BF16 = 0
 MODE_KVI8R = 1
-MODES = {"exact": MODE_EXACT_BF16, "bf16": MODE_EXACT_BF16, "kvi8r": MODE_KVI8R}
+MODE_KVI8R32 = 2  # kvi8r with one fp16 scale per 32 rotated values
+MODES = {"exact": MODE_EXACT_BF16, "bf16": MODE_EXACT_BF16, "kvi8r": MODE_KVI8R, "kvi8r32": MODE_KVI8R32}
 SOL = 0x100  # H3A_SOL: dropped tiles of a tile_mask enter as one pseudo-key each
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libh3a.so")
@@ -57,6 +59,8 @@ def _load():
     lib.h3a_last_error.argtypes = []
     lib.h3a_kv_quantize.restype = i32
     lib.h3a_kv_quantize.argtypes = [vp, i64, i64, i32, i32, i64, i64, vp, vp, vp]
+    lib.h3a_kv_quantize_g32.restype = i32
+    lib.h3a_kv_quantize_g32.argtypes = [vp, i64, i64, i32, i32, i64, i64, vp, vp, vp]
     lib.h3a_attention_workspace_bytes.restype = sz
     lib.h3a_attention_workspace_bytes.argtypes = [i64, i64, i32, i32, i64, i32, i32]
     lib.h3a_attention.restype = i32
@@ -112,25 +116,33 @@ def h3a_abi_version() -> int:
 def h3a_kv_quantize(x, codes, scales, token_offset: int = 0, stream=None):
     """Quantise x (bf16 [n_tokens, n_heads, 128], rows contiguous) into rows
     [token_offset, token_offset + n_tokens) of a kvi8r store: codes int8
-    [n_heads, s_total, 128] and scales fp16 [n_heads, s_total]."""
+    [n_heads, s_total, 128] and scales fp16 [n_heads, s_total] (one per row,
+    h3a_kv_quantize) or [n_heads, s_total, 4] (one per 32 values, the kvi8r32
+    store, h3a_kv_quantize_g32)."""
     lib = _load()
     _need(x, "x", torch.bfloat16)
     _need(codes, "codes", torch.int8)
     _need(scales, "scales", torch.float16)
     if x.dim() != 3 or x.stride(2) != 1 or (x.shape[1] > 1 and x.stride(1) != x.shape[2]):
         raise ValueError("x must be [n_tokens, n_heads, head_dim] with contiguous (token, head) rows")
-    if codes.dim() != 3 or not codes.is_contiguous() or scales.dim() != 2 or not scales.is_contiguous():
-        raise ValueError("codes must be contiguous [n_heads, s_total, 128] and scales contiguous [n_heads, s_total]")
+    grouped = scales.dim() == 3
+    if codes.dim() != 3 or not codes.is_contiguous() or scales.dim() not in (2, 3) or not scales.is_contiguous() \
+            or (grouped and scales.shape[2] != 4):
+        raise ValueError("codes must be contiguous [n_heads, s_total, 128] and scales contiguous "
+                         "[n_heads, s_total] or [n_heads, s_total, 4]")
     stride = x.stride(0) if x.shape[0] > 1 else x.shape[1] * x.shape[2]
-    _check(lib.h3a_kv_quantize(_ptr(x), stride, x.shape[0], x.shape[1], x.shape[2], int(token_offset),
-                               codes.shape[1], _ptr(codes), _ptr(scales), _stream(x, stream)))
+    fn = lib.h3a_kv_quantize_g32 if grouped else lib.h3a_kv_quantize
+    _check(fn(_ptr(x), stride, x.shape[0], x.shape[1], x.shape[2], int(token_offset), codes.shape[1], _ptr(codes),
+              _ptr(scales), _stream(x, stream)))
 
 
-def new_kvi8r_store(s_total: int, n_heads: int, device="cuda"):
-    """Allocate an empty kvi8r store: (k_codes, v_codes, scales[2, n_heads, s_total])."""
+def new_kvi8r_store(s_total: int, n_heads: int, device="cuda", per32: bool = False):
+    """Allocate an empty kvi8r store: (k_codes, v_codes, scales[2, n_heads, s_total]), or with per32 the
+    kvi8r32 store, scales[2, n_heads, s_total, 4]."""
     k = torch.empty((n_heads, s_total, HEAD_DIM), dtype=torch.int8, device=device)
     v = torch.empty((n_heads, s_total, HEAD_DIM), dtype=torch.int8, device=device)
-    s = torch.empty((2, n_heads, s_total), dtype=torch.float16, device=device)
+    shape = (2, n_heads, s_total, 4) if per32 else (2, n_heads, s_total)
+    s = torch.empty(shape, dtype=torch.float16, device=device)
     return k, v, s
 
 
@@ -147,6 +159,7 @@ def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: i
 
     mode "exact": k_store / v_store bf16 [s_kv, H, 128], scales None.
     mode "kvi8r": k_store / v_store int8 [H, s_kv, 128], scales fp16 [2, H, s_kv].
+    mode "kvi8r32": k_store / v_store int8 [H, s_kv, 128], scales fp16 [2, H, s_kv, 4].
     tile_mask: None (dense) or uint8 [H, ceil(s_q/64), ceil(s_kv/64)].
     sol: with a tile_mask, each dropped tile enters as one pseudo-key (tile-mean K and V, weight = its key count).
     workspace: a uint8 GPU tensor of at least h3a_attention_workspace_bytes; allocated here when None.
@@ -159,10 +172,12 @@ def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: i
     if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be contiguous [s_q, n_heads, head_dim] tensors of equal shape")
     s_q, n_heads, head_dim = q.shape
-    if mode == MODE_KVI8R:
+    if mode in (MODE_KVI8R, MODE_KVI8R32):
         _need(k_store, "k_store", torch.int8)
         _need(v_store, "v_store", torch.int8)
         _need(scales, "scales", torch.float16)
+        if scales.dim() != (4 if mode == MODE_KVI8R32 else 3):
+            raise ValueError("scales must be [2, H, s_kv] (kvi8r) or [2, H, s_kv, 4] (kvi8r32)")
         s_kv = k_store.shape[1]
     else:
         _need(k_store, "k_store", torch.bfloat16)

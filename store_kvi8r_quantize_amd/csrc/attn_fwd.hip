@@ -28,7 +28,9 @@
 //     V rows then get one packed multiply by their scale.  K stays as exact
 //     integer codes and each key's scale (times softmax_scale * log2 e) is
 //     applied to that key's fp32 score, which keeps the fp16 rounding of
-//     code * scale out of the scores.
+//     code * scale out of the scores.  The kvi8r32 store (one scale per 32
+//     values, "Low VRAM, low RAM", "What is next") has four scales per key, so
+//     its K is dequantised to fp16 in LDS like V.
 //   * LDS: K [key][dim] and V^T [dim][key], rows padded so fragment reads are
 //     bank-conflict free; triple-buffered in the dense kernel (102 KB),
 //     double-buffered in the sparse one.
@@ -74,6 +76,8 @@ struct Operand<1> {  // kvi8r store: fp16 operands
   }
   static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
 };
+template <>
+struct Operand<2> : Operand<1> {};  // kvi8r32 store (one scale per 32 values): fp16 operands
 
 // int8 codes -> fp16.  For u = code ^ 0x80 (= code + 128 as an unsigned byte),
 // the fp16 bit pattern 0x64 << 8 | u is 1024 + u; subtracting 1152 leaves the
@@ -133,15 +137,17 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
       st.k[j][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, o + 16, 0, 0));
     }
   } else {
+    constexpr int G = MODE == 2 ? 4 : 1;  // scales per row
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
     const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, left * kHeadDim);
-    const auto rks = make_rsrc(a.k_scale + hrow, left * 2);
+    const auto rks = make_rsrc(a.k_scale + hrow * G, left * 2 * G);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
       const int u = tid + NT * j;
       st.k[j][0] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (u >> 3) * kHeadDim + 16 * (u & 7), 0, 0));
-      st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, (u >> 3) * 2, 0, 0);
+      // kvi8r: the key's scale; kvi8r32: the scale of the unit's 32-value group (dims 16*(u&7)..)
+      st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, ((u >> 3) * G + (MODE == 2 ? (u & 7) >> 1 : 0)) * 2, 0, 0);
     }
   }
 }
@@ -166,9 +172,10 @@ __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk
       }
     }
   } else {
+    constexpr int G = MODE == 2 ? 4 : 1;  // scales per row
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
     const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, left * kHeadDim);
-    const auto rvs = make_rsrc(a.v_scale + hrow, left * 2);
+    const auto rvs = make_rsrc(a.v_scale + hrow * G, left * 2 * G);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
@@ -176,7 +183,15 @@ __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         st.v[j][r][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, (r0 + r) * kHeadDim + 4 * (u & 31), 0, 0);
-      if (left >= kTile && (hrow & 3) == 0) {  // whole tile in range, 8-byte aligned: the 4 scales in one load
+      if constexpr (MODE == 2) {  // the 4 keys' scales of this unit's 32-value group, one load each
+        const int grp = (u & 31) >> 3;
+        const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 0) * 4 + grp) * 2, 0, 0);
+        const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 1) * 4 + grp) * 2, 0, 0);
+        const uint32_t s2 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 2) * 4 + grp) * 2, 0, 0);
+        const uint32_t s3 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 3) * 4 + grp) * 2, 0, 0);
+        st.vs[j][0] = (s0 & 0xFFFFu) | (s1 << 16);
+        st.vs[j][1] = (s2 & 0xFFFFu) | (s3 << 16);
+      } else if (left >= kTile && (hrow & 3) == 0) {  // whole tile in range, 8-byte aligned: the 4 scales in one load
         const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, r0 * 2, 0, 0));
         st.vs[j][0] = w[0];
         st.vs[j][1] = w[1];
@@ -221,13 +236,23 @@ __device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t
     if constexpr (MODE == 0) {
       c0 = st.k[j][0];
       c1 = st.k[j][1];
-    } else {
+    } else if constexpr (MODE == 1) {
       const u32x4 w = st.k[j][0];
       const uint32_t u0 = w[0] ^ 0x80808080u, u1 = w[1] ^ 0x80808080u;
       const uint32_t u2 = w[2] ^ 0x80808080u, u3 = w[3] ^ 0x80808080u;
       c0 = u32x4{code_pair(u0, kSelLo), code_pair(u0, kSelHi), code_pair(u1, kSelLo), code_pair(u1, kSelHi)};
       c1 = u32x4{code_pair(u2, kSelLo), code_pair(u2, kSelHi), code_pair(u3, kSelLo), code_pair(u3, kSelHi)};
       if (d16 == 0) lc[r] = (float)__builtin_bit_cast(_Float16, (uint16_t)st.ks[j]) * sl2;
+    } else {  // kvi8r32: a key has four scales, so K is dequantised to fp16 here like V
+      const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.ks[j]);
+      const half2v s2 = {sc, sc};
+      const u32x4 w = st.k[j][0];
+      const uint32_t u0 = w[0] ^ 0x80808080u, u1 = w[1] ^ 0x80808080u;
+      const uint32_t u2 = w[2] ^ 0x80808080u, u3 = w[3] ^ 0x80808080u;
+      c0 = u32x4{dequant_pair(u0, kSelLo, s2), dequant_pair(u0, kSelHi, s2), dequant_pair(u1, kSelLo, s2),
+                 dequant_pair(u1, kSelHi, s2)};
+      c1 = u32x4{dequant_pair(u2, kSelLo, s2), dequant_pair(u2, kSelHi, s2), dequant_pair(u3, kSelLo, s2),
+                 dequant_pair(u3, kSelHi, s2)};
     }
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16) = c0;
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
@@ -410,7 +435,8 @@ __device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
 }
 
 // Score factors of this lane's keys 32*kb + 8*jg + 4g + {0..3}: key scale *
-// softmax_scale * log2 e (kvi8r, from LDS) or softmax_scale * log2 e (exact).
+// softmax_scale * log2 e (kvi8r, from LDS) or softmax_scale * log2 e (exact,
+// and kvi8r32, whose K is dequantised in LDS).
 // Pseudo-key tiles (Sol residual) take theirs from LDS in both modes, and also
 // a per-key additive term, log2 of the key's multiplicity, from lc + kTile.
 template <int MODE, bool PSEUDO = false>
@@ -447,14 +473,14 @@ __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float 
         p[e] = __builtin_amdgcn_exp2f(x);
       }
       const uint32_t q01 = Op::pack(p[0], p[1]), q23 = Op::pack(p[2], p[3]);
-      if constexpr (MODE == 1)
+      if constexpr (MODE != 0)
         hs[4 * kb + jg] = __builtin_bit_cast(half2v, q01) + __builtin_bit_cast(half2v, q23);
       else
         gs[4 * kb + jg] = (p[0] + p[1]) + (p[2] + p[3]);
       rb.pf[kb][jg >> 1][2 * (jg & 1)] = q01;
       rb.pf[kb][jg >> 1][2 * (jg & 1) + 1] = q23;
     }
-  if constexpr (MODE == 1) {
+  if constexpr (MODE != 0) {
     const half2v h = ((hs[0] + hs[1]) + (hs[2] + hs[3])) + ((hs[4] + hs[5]) + (hs[6] + hs[7]));
     return (float)h[0] + (float)h[1];
   } else {
@@ -833,11 +859,12 @@ __global__ __launch_bounds__(256) void tile_means_kernel(const void* __restrict_
     const uint16_t* src = static_cast<const uint16_t*>(is_v ? v : k) + (r0 * n_heads + head) * kHeadDim + d;
     for (int r = 0; r < n; ++r) sum += bf16lo_to_f32(src[(int64_t)r * n_heads * kHeadDim]);
   } else {
+    constexpr int G = MODE == 2 ? 4 : 1;  // scales per row; dimension d uses scale d / 32 of kvi8r32
     const int64_t hr = (int64_t)head * s_kv + r0;
     const int8_t* src = static_cast<const int8_t*>(is_v ? v : k) + hr * kHeadDim + d;
-    const uint16_t* sc = (is_v ? v_scale : k_scale) + hr;
+    const uint16_t* sc = (is_v ? v_scale : k_scale) + hr * G + (G == 4 ? d >> 5 : 0);
     for (int r = 0; r < n; ++r)
-      sum += (float)src[(int64_t)r * kHeadDim] * (float)__builtin_bit_cast(_Float16, sc[r]);
+      sum += (float)src[(int64_t)r * kHeadDim] * (float)__builtin_bit_cast(_Float16, sc[r * G]);
   }
   const float mean = sum / (float)n;
   const int64_t o = ((int64_t)head * n_kt + t) * kHeadDim + d;
@@ -891,7 +918,8 @@ hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, const SolA
   static_assert(kSparseBlockRows == 2 * 32, "sparse kernel covers one routing tile");
   if (sol != nullptr && (!sparse || a.s_kv > kSolMaxKv)) return hipErrorInvalidValue;
   if (mode == 0) return sparse ? launch_sparse<0>(a, sol, stream) : launch_dense<0>(a, stream);
-  return sparse ? launch_sparse<1>(a, sol, stream) : launch_dense<1>(a, stream);
+  if (mode == 1) return sparse ? launch_sparse<1>(a, sol, stream) : launch_dense<1>(a, stream);
+  return sparse ? launch_sparse<2>(a, sol, stream) : launch_dense<2>(a, stream);
 }
 
 hipError_t launch_route_build(const uint8_t* mask, int64_t n_qt_total, int64_t qt0, int32_t n_qt, int32_t n_kt,
@@ -912,8 +940,11 @@ hipError_t launch_tile_means(int mode, const void* k, const void* v, const uint1
   if (mode == 0)
     hipLaunchKernelGGL(tile_means_kernel<0>, grid, dim3(256), 0, stream, k, v, k_scale, v_scale, s_kv, n_heads,
                        kmean, vmean, kmscale);
-  else
+  else if (mode == 1)
     hipLaunchKernelGGL(tile_means_kernel<1>, grid, dim3(256), 0, stream, k, v, k_scale, v_scale, s_kv, n_heads,
+                       kmean, vmean, kmscale);
+  else
+    hipLaunchKernelGGL(tile_means_kernel<2>, grid, dim3(256), 0, stream, k, v, k_scale, v_scale, s_kv, n_heads,
                        kmean, vmean, kmscale);
   return hipGetLastError();
 }

@@ -97,7 +97,7 @@ bool workspace_layout(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chun
     w->kmscale = off;
     off = align256(off + (uint64_t)(n_kt * n_heads) * 4);
   }
-  if (mode == H3A_MODE_KVI8R) {
+  if (mode != H3A_MODE_EXACT_BF16) {
     w->qrot = off;
     off = align256(off + (uint64_t)elems * 2);
     w->orot = off;
@@ -154,12 +154,13 @@ int check_store(int32_t mode, const void* k, const void* v, const void* scales, 
                 const char* k_name, const char* v_name) {
   int64_t n;
   if (!mul_ok(s_kv, (int64_t)n_heads * H3A_HEAD_DIM, &n)) return fail(H3A_EINVAL, "size overflow");
-  const bool q8 = mode == H3A_MODE_KVI8R;
+  const bool q8 = mode != H3A_MODE_EXACT_BF16;
   const uint64_t bytes = (uint64_t)n * (q8 ? 1 : 2);
   int rc;
   if ((rc = check_buffer(k, bytes, 16, k_name)) != H3A_OK) return rc;
   if ((rc = check_buffer(v, bytes, 16, v_name)) != H3A_OK) return rc;
-  if (q8) return check_buffer(scales, (uint64_t)s_kv * n_heads * 4, 2, "scales");
+  if (mode == H3A_MODE_KVI8R) return check_buffer(scales, (uint64_t)s_kv * n_heads * 4, 2, "scales");
+  if (mode == H3A_MODE_KVI8R32) return check_buffer(scales, (uint64_t)s_kv * n_heads * 16, 8, "scales");
   return H3A_OK;
 }
 
@@ -202,9 +203,9 @@ Pass make_pass(int32_t mode, const void* q, void* out, const void* k, const void
   p.out = static_cast<uint16_t*>(out);
   p.k = k;
   p.v = v;
-  if (mode == H3A_MODE_KVI8R) {
+  if (mode != H3A_MODE_EXACT_BF16) {
     p.k_scale = static_cast<const uint16_t*>(scales);
-    p.v_scale = p.k_scale + s_kv * n_heads;
+    p.v_scale = p.k_scale + s_kv * n_heads * (mode == H3A_MODE_KVI8R32 ? 4 : 1);
   }
   p.s_q = s_q;
   p.s_kv = s_kv;
@@ -236,7 +237,7 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
     a.k = p.k;
     a.v = p.v;
     hipError_t e;
-    if (p.mode == H3A_MODE_KVI8R) {
+    if (p.mode != H3A_MODE_EXACT_BF16) {
       uint16_t* qrot = reinterpret_cast<uint16_t*>(p.ws + p.wl.qrot);
       if ((e = h3a::launch_rotate_q(p.q + off, qrot, rows * p.n_heads, p.st)) != hipSuccess)
         return hip_fail(e, "rotate_q launch");
@@ -278,7 +279,7 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
       std::lock_guard<std::mutex> lk(g_timing_mu);
       g_events.emplace_back(ev0, ev1);
     }
-    if (p.mode == H3A_MODE_KVI8R) {
+    if (p.mode != H3A_MODE_EXACT_BF16) {
       if ((e = h3a::launch_unrotate_o(reinterpret_cast<const float*>(p.ws + p.wl.orot), p.out + off,
                                       rows * p.n_heads, p.st)) != hipSuccess)
         return hip_fail(e, "unrotate_o launch");
@@ -287,16 +288,9 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
   return H3A_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t h3a_abi_version(void) { return H3A_ABI_VERSION; }
-
-const char* h3a_last_error(void) { return g_err.c_str(); }
-
-int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
-                        int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16, void* stream) {
+// One quantize call; grouped: one scale per 32 values.
+int kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16, bool grouped, void* stream) {
   g_err.clear();
   if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
   if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
@@ -310,19 +304,40 @@ int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens,
                 (long long)x_token_stride);
   if (n_tokens == 0) return H3A_OK;
   if (n_tokens > INT32_MAX / 2 || s_total > (int64_t)1 << 40) return fail(H3A_EINVAL, "sizes too large");
+  const int64_t g = grouped ? 4 : 1;
   int64_t xb, cb, sb;
   if (!mul_ok(n_tokens - 1, x_token_stride, &xb) || !mul_ok(s_total * n_heads, H3A_HEAD_DIM, &cb) ||
-      !mul_ok(s_total, (int64_t)n_heads * 2, &sb))
+      !mul_ok(s_total, (int64_t)n_heads * 2 * g, &sb))
     return fail(H3A_EINVAL, "size overflow");
   xb = (xb + (int64_t)n_heads * H3A_HEAD_DIM) * 2;
   int rc;
   if ((rc = check_buffer(x, (uint64_t)xb, 16, "x")) != H3A_OK) return rc;
   if ((rc = check_buffer(codes, (uint64_t)cb, 16, "codes")) != H3A_OK) return rc;
-  if ((rc = check_buffer(scales_f16, (uint64_t)sb, 2, "scales")) != H3A_OK) return rc;
+  if ((rc = check_buffer(scales_f16, (uint64_t)sb, grouped ? 8 : 2, "scales")) != H3A_OK) return rc;
   hipError_t e = h3a::launch_kvi8r_quantize(static_cast<const uint16_t*>(x), x_token_stride, n_tokens, n_heads,
                                             token_offset, s_total, codes, static_cast<uint16_t*>(scales_f16),
-                                            static_cast<hipStream_t>(stream));
+                                            grouped, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3A_OK : hip_fail(e, "kvi8r_quantize launch");
+}
+}  // namespace
+
+extern "C" {
+
+int32_t h3a_abi_version(void) { return H3A_ABI_VERSION; }
+
+const char* h3a_last_error(void) { return g_err.c_str(); }
+
+int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                        int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16, void* stream) {
+  return kv_quantize(x, x_token_stride, n_tokens, n_heads, head_dim, token_offset, s_total, codes, scales_f16, false,
+                     stream);
+}
+
+int32_t h3a_kv_quantize_g32(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads,
+                            int32_t head_dim, int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16,
+                            void* stream) {
+  return kv_quantize(x, x_token_stride, n_tokens, n_heads, head_dim, token_offset, s_total, codes, scales_f16, true,
+                     stream);
 }
 
 size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, int64_t q_chunk,
@@ -330,7 +345,8 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
   if (head_dim != H3A_HEAD_DIM || n_heads < 1 || s_kv < 0) return 0;
   const bool sol = (mode & H3A_SOL) != 0;
   mode &= ~H3A_SOL;
-  if ((mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R) || (sol && !sparse)) return 0;
+  if ((mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32) || (sol && !sparse))
+    return 0;
   WorkspaceLayout w;
   if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse != 0, sol, &w)) return 0;
   return (size_t)w.total;
@@ -345,7 +361,8 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
   const bool sol = (mode & H3A_SOL) != 0;
   const int32_t mode_arg = mode;
   mode &= ~H3A_SOL;
-  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R) return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
+  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32)
+    return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
   if (sol && tile_mask == nullptr) return fail(H3A_EINVAL, "H3A_SOL needs a tile_mask");
   if (sol && s_kv > h3a::kSolMaxKv) return fail(H3A_EINVAL, "H3A_SOL supports s_kv up to 2^30 - 64");
   int rc;
@@ -353,8 +370,8 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
   const bool sparse = tile_mask != nullptr;
   if (sparse && q_chunk % H3A_TILE != 0)
     return fail(H3A_EINVAL, "q_chunk must be a multiple of 64 with a tile_mask (got %lld)", (long long)q_chunk);
-  if (mode == H3A_MODE_KVI8R && scales == nullptr && s_kv > 0)
-    return fail(H3A_EINVAL, "kvi8r mode needs scales");
+  if (mode != H3A_MODE_EXACT_BF16 && scales == nullptr && s_kv > 0)
+    return fail(H3A_EINVAL, "kvi8r modes need scales");
   if (mode == H3A_MODE_EXACT_BF16 && scales != nullptr) return fail(H3A_EINVAL, "exact mode takes no scales");
   if (s_q == 0) return H3A_OK;
 

@@ -6,6 +6,11 @@
 // orthonormal Hadamard basis, take its absmax, store fp16(absmax/127) and the
 // int8 codes of the row against that stored scale.
 //
+// GROUPED: the per-32-value variant ("Low VRAM, low RAM", "What is next": a
+// scale per 32 values, finer than per row).  Each group of 32 consecutive
+// rotated values gets its own fp16 scale and its codes are taken against it;
+// scales are stored [n_heads, s_total, 4].
+//
 // Layout on MI355X: one workgroup = 4 waves = 64 tokens of one head; a row is
 // handled by 4 lanes holding 32 values each, so 5 of the 7 butterfly stages
 // stay in registers and 2 use quad DPP moves.  Loads are 64 contiguous bytes
@@ -20,6 +25,7 @@ namespace {
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds |x| < 2^22 to an integer, ties to even
 
+template <bool GROUPED>
 __global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __restrict__ x,
                                                              int64_t x_token_stride, int64_t n_tokens,
                                                              int64_t token_offset, int64_t s_total,
@@ -49,16 +55,29 @@ __global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __r
   fwht32_in_lane(v);
   fwht32_cross_lane(v, sub);  // v now holds y * sqrt(128)
 
-  float a = 0.0f;
+  // Absmax of the row (one group) or of each 32-value group k = elements
+  // 32k..32k+31, held as v[8k..8k+7] on the quad's four lanes.
+  constexpr int NG = GROUPED ? 4 : 1;
+  float a[NG];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
-  a = fmaxf(a, dpp_f32<kDppXor1>(a));
-  a = fmaxf(a, dpp_f32<kDppXor2>(a));
+  for (int gi = 0; gi < NG; ++gi) a[gi] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a[GROUPED ? i >> 3 : 0] = fmaxf(a[GROUPED ? i >> 3 : 0], fabsf(v[i]));
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    a[gi] = fmaxf(a[gi], dpp_f32<kDppXor1>(a[gi]));
+    a[gi] = fmaxf(a[gi], dpp_f32<kDppXor2>(a[gi]));
+  }
 
   // scale = fp16(max|y| / 127) from the (exact) fp32 absmax, in fp64; then the
   // reciprocal that maps unnormalised values onto the code grid.
-  const uint32_t sbits = f64_to_f16_rne_sat((double)a * kInv127Sqrt128);
-  const float r = sbits ? (float)(1.0 / (f16_bits_to_f64(sbits) * kSqrt128)) : 0.0f;
+  uint32_t sbits[NG];
+  float r[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    sbits[gi] = f64_to_f16_rne_sat((double)a[gi] * kInv127Sqrt128);
+    r[gi] = sbits[gi] ? (float)(1.0 / (f16_bits_to_f64(sbits[gi]) * kSqrt128)) : 0.0f;
+  }
 
   // code = clamp(round-half-even(y / s)): one fused multiply-add with the magic
   // constant rounds the exact product once; med3 clamps to [-127, 127].
@@ -68,7 +87,7 @@ __global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __r
     uint32_t b[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float f = __builtin_fmaf(v[4 * i + j], r, kMagic);
+      float f = __builtin_fmaf(v[4 * i + j], r[GROUPED ? i >> 1 : 0], kMagic);
       f = __builtin_amdgcn_fmed3f(f, kMagic - 127.0f, kMagic + 127.0f);
       b[j] = __float_as_uint(f);
     }
@@ -85,7 +104,12 @@ __global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __r
       u32x2 w = {packed[2 * k], packed[2 * k + 1]};
       *reinterpret_cast<u32x2*>(dst + 32 * k + 8 * sub) = w;
     }
-    if (sub == 0) scales[row] = (uint16_t)sbits;
+    if constexpr (GROUPED) {
+      if (sub == 0)
+        *reinterpret_cast<u32x2*>(scales + row * 4) = u32x2{sbits[0] | (sbits[1] << 16), sbits[2] | (sbits[3] << 16)};
+    } else {
+      if (sub == 0) scales[row] = (uint16_t)sbits[0];
+    }
   }
 }
 
@@ -93,11 +117,15 @@ __global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __r
 
 hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int64_t n_tokens,
                                  int32_t n_heads, int64_t token_offset, int64_t s_total, int8_t* codes,
-                                 uint16_t* scales, hipStream_t stream) {
+                                 uint16_t* scales, bool grouped, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
   dim3 grid((unsigned)((n_tokens + 63) / 64), (unsigned)n_heads);
-  hipLaunchKernelGGL(kvi8r_quantize_kernel, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
-                     token_offset, s_total, codes, scales);
+  if (grouped)
+    hipLaunchKernelGGL(kvi8r_quantize_kernel<true>, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
+                       token_offset, s_total, codes, scales);
+  else
+    hipLaunchKernelGGL(kvi8r_quantize_kernel<false>, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
+                       token_offset, s_total, codes, scales);
   return hipGetLastError();
 }
 

@@ -8,9 +8,10 @@
 
 namespace h3a {
 
+// grouped: one scale per 32 rotated values, scales [n_heads, s_total, 4]; else one per row [n_heads, s_total].
 hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int64_t n_tokens,
                                  int32_t n_heads, int64_t token_offset, int64_t s_total, int8_t* codes,
-                                 uint16_t* scales, hipStream_t stream);
+                                 uint16_t* scales, bool grouped, hipStream_t stream);
 
 hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
 hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
@@ -18,9 +19,9 @@ hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, hipStr
 // One query chunk of attention.
 struct AttnChunk {
   const uint16_t* q;       // exact: bf16 Q rows [rows, H, 128]; kvi8r: rotated fp16 Q' [rows, H, 128]
-  const void* k;           // exact: bf16 [s_kv, H, 128]; kvi8r: int8 codes [H, s_kv, 128]
+  const void* k;           // exact: bf16 [s_kv, H, 128]; kvi8r, kvi8r32: int8 codes [H, s_kv, 128]
   const void* v;
-  const uint16_t* k_scale; // kvi8r: fp16 [H, s_kv]
+  const uint16_t* k_scale; // kvi8r: fp16 [H, s_kv]; kvi8r32: fp16 [H, s_kv, 4]
   const uint16_t* v_scale;
   void* out;               // exact: bf16 [rows, H, 128]; kvi8r: fp32 O' (normalised, rotated) [rows, H, 128]
   const int32_t* counts;   // sparse: kept-tile count per (head, 64-row q-tile) of the chunk

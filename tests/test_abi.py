@@ -54,6 +54,8 @@ def _attn(lib, **kw):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(head_dim=64), -2, "head_dim"),
     (dict(mode=7), -1, "mode"),
+    (dict(mode=3), -1, "mode"),
+    (dict(mode=2, scales=None), -1, "scales"),
     (dict(n_heads=0), -1, "n_heads"),
     (dict(s_q=-1), -1, "s_q"),
     (dict(q_chunk=0), -1, "q_chunk"),
@@ -132,10 +134,18 @@ def test_quantize_zero_tokens_is_noop(lib):
     assert lib.h3a_kv_quantize(None, 256, 0, 2, 128, 0, 0, None, None, None) == 0
 
 
+def test_quantize_g32_rejects_bad_arguments(lib):
+    assert lib.h3a_kv_quantize_g32(None, 256, 64, 2, 96, 0, 64, None, None, None) == -2
+    assert lib.h3a_kv_quantize_g32(None, 256, 64, 2, 128, 10, 64, None, None, None) == -1
+    assert "exceeds" in lib.h3a_last_error().decode()
+    assert lib.h3a_kv_quantize_g32(None, 256, 0, 2, 128, 0, 0, None, None, None) == 0
+
+
 def test_workspace_sizes(lib):
     # kvi8r: rotated Q (fp16) + rotated output (fp32) for one chunk of rows
     assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "kvi8r", False) == 256 * 2 * 128 * 6
     assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "exact", False) == 0
+    assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "kvi8r32", False) == 256 * 2 * 128 * 6
     assert h3a.h3a_attention_workspace_bytes(100, 1024, 2, 256, "kvi8r", False) == 100 * 2 * 128 * 6
     # sparse adds per-(head, q-tile) counts and kept lists
     dense = h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "exact", True)

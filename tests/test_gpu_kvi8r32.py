@@ -1,0 +1,182 @@
+"""GPU parity of the per-32-value kvi8r store ("kvi8r32"): h3a_kv_quantize_g32 and
+h3a_attention in H3A_MODE_KVI8R32, through the C ABI, against the oracle.
+
+"Low VRAM, low RAM" page, "What is next": a kvi8r variant with one scale per 32
+values, finer than per row.  Quantisation: codes equal the oracle's with at most
+1e-4 off by one (rounding ties), scales within 1 fp16 ulp, closed form exact,
+chunked build bitwise.  Attention: the tolerances of kvi8r (relative L2 <= 2e-3,
+max abs <= 1e-2 against the oracle on the same store), q_chunk bitwise, all-ones
+mask == dense bitwise, the Sol arm against its oracle; and on outlier keys the
+finer store lands closer to unquantised attention than the per-row store.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import store_kvi8r_quantize_amd as h3a
+import synth
+from gpu_common import (KVI8R_MAX_ABS, KVI8R_REL_L2, SCALE, CODE_MISMATCH, gpu_inputs, gpu_u16, host_u16, rel_l2,
+                        say)
+
+pytestmark = pytest.mark.gpu
+
+
+def _store32(k, v, kv_chunk=None):
+    s, nh, _ = k.shape
+    kc, vc, sc = h3a.new_kvi8r_store(s, nh, per32=True)
+    step = kv_chunk or max(s, 1)
+    for t0 in range(0, s, step):
+        h3a.h3a_kv_quantize(k[t0:t0 + step], kc, sc[0], token_offset=t0)
+        h3a.h3a_kv_quantize(v[t0:t0 + step], vc, sc[1], token_offset=t0)
+    torch.cuda.synchronize()
+    return kc, vc, sc
+
+
+def _head(store, h):
+    kc, vc, sc = store
+    return kc[h].cpu().numpy(), host_u16(sc[0, h]), vc[h].cpu().numpy(), host_u16(sc[1, h])
+
+
+def test_closed_form_one_spike_per_group():
+    ks, pos, sign = [0, -1, 2, -3], [3, 40, 81, 127], [1, -1, 1, -1]
+    y = np.zeros((1, 128))
+    for k, p, sg in zip(ks, pos, sign):
+        y[0, p] = sg * 127.0 * 2.0 ** k
+    x = (y @ oracle.orthonormal_hadamard()).astype(np.float32)
+    xb = synth.bf16_bits_from_f32(x)[:, None, :]
+    # bf16 rounding of x moves y slightly; compare with the oracle on the same bf16 row
+    codes_o, s_o, _ = oracle.quantize_rows_grouped(oracle.bf16_to_f64(xb[:, 0]))
+    g = gpu_u16(xb)
+    codes = torch.empty((1, 1, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((1, 1, 4), dtype=torch.float16, device="cuda")
+    h3a.h3a_kv_quantize(g, codes, scales)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(scales)[0], s_o)
+    assert np.array_equal(codes.cpu().numpy()[0], codes_o)
+
+
+@pytest.mark.parametrize("name", ["tiny", "outlier16k"])
+@pytest.mark.parametrize("tensor", ["k", "v"])
+def test_codes_and_scales_match_oracle(name, tensor):
+    w = synth.WORKLOADS[name]
+    bits = synth.qkv_bf16(w, (tensor,))[tensor]
+    x = gpu_u16(bits)
+    n, nh = w.seq, w.heads
+    codes = torch.empty((nh, n, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((nh, n, 4), dtype=torch.float16, device="cuda")
+    h3a.h3a_kv_quantize(x, codes, scales)
+    torch.cuda.synchronize()
+    cg, sg = codes.cpu().numpy(), host_u16(scales)
+    for h in range(0, nh, max(nh // 4, 1)):
+        c_o, s_o, y = oracle.quantize_rows_grouped(oracle.bf16_to_f64(bits[:, h]))
+        ulp = np.abs(sg[h].astype(np.int64) - s_o.astype(np.int64)).max()
+        # codes against the GPU's own scales (the decision the kernel takes), and against the oracle's
+        same = oracle.codes_for_scales(y.reshape(-1, 32), sg[h].reshape(-1)).reshape(n, 128)
+        d_same = np.count_nonzero(cg[h] != same) / cg[h].size
+        d_own = np.count_nonzero(cg[h] != c_o) / cg[h].size
+        say(name, tensor, "head", h, "scale max ulp", ulp, "codes off (same scale)", d_same, "(own)", d_own)
+        assert ulp <= 1
+        assert np.abs(cg[h].astype(np.int64) - same).max() <= 1 and d_same <= CODE_MISMATCH
+        assert d_own <= CODE_MISMATCH
+
+
+def test_chunked_build_equals_one_shot():
+    w = synth.WORKLOADS["tiny"]
+    bits = synth.qkv_bf16(w, ("k",))["k"]
+    x = gpu_u16(bits)
+    a = _store32(x, x)
+    b = _store32(x, x, kv_chunk=300)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[2].view(torch.int16), b[2].view(torch.int16))
+
+
+def _attend(q, store, q_chunk, mask=None, sol=False):
+    out = torch.empty_like(q)
+    h3a.h3a_attention(q, *store, out, q_chunk=q_chunk, mode="kvi8r32", tile_mask=mask, sol=sol)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_rows(bits_q, store, out, heads, rows_of, tag, ref_fn=None):
+    got_all, ref_all = [], []
+    for h in heads:
+        rows = rows_of(h)
+        kc, ks, vc, vs = _head(store, h)
+        q = oracle.bf16_to_f64(bits_q(h)[rows])
+        ref = ref_fn(h, rows, q, kc, ks, vc, vs) if ref_fn else oracle.kvi8r_attention(q, kc, ks, vc, vs, SCALE)
+        got_all.append(oracle.bf16_to_f64(host_u16(out[torch.from_numpy(rows).cuda(), h])))
+        ref_all.append(ref)
+    got, ref = np.concatenate(got_all), np.concatenate(ref_all)
+    r, mx = rel_l2(got, ref), float(np.abs(got - ref).max())
+    say(tag, "kvi8r32 relL2", r, "max abs", mx)
+    assert r <= KVI8R_REL_L2 and mx <= KVI8R_MAX_ABS
+
+
+@pytest.mark.parametrize("name,q_chunk", [("tiny", 256), ("outlier16k", 4096)])
+def test_attention_matches_oracle(name, q_chunk):
+    w = synth.WORKLOADS[name]
+    bits = synth.qkv_bf16(w)
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    store = _store32(g["k"], g["v"])
+    out = _attend(g["q"], store, q_chunk)
+    rows_of = (lambda h: np.arange(w.seq)) if name == "tiny" else (lambda h: synth.sampled_rows(w, h, 256))
+    _check_rows(lambda h: bits["q"][:, h], store, out, range(w.heads), rows_of, name)
+    # every row depends on that row alone: other chunkings give the same bits
+    out2 = _attend(g["q"], store, 64 if name == "tiny" else 1000)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+@pytest.mark.parametrize("s,s_kv,heads,q_chunk", [(1000, 777, 3, 300), (65, 1, 2, 64)])
+def test_ragged_shapes(s, s_kv, heads, q_chunk):
+    w = synth.Workload("ragged32", max(s, s_kv), heads, 41, 256, 0)
+    bits = synth.qkv_bf16(w)
+    q = gpu_u16(bits["q"][:s])
+    store = _store32(gpu_u16(bits["k"][:s_kv]), gpu_u16(bits["v"][:s_kv]))
+    out = _attend(q, store, q_chunk)
+    _check_rows(lambda h: bits["q"][:s, h], store, out, range(heads), lambda h: np.arange(s), "ragged32")
+
+
+def test_all_ones_mask_equals_dense_bitwise_and_sol_matches_oracle():
+    w = synth.Workload("masked32", 1000, 2, 12, 256, 0)
+    bits = synth.qkv_bf16(w)
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    store = _store32(g["k"], g["v"])
+    nt = w.n_tiles
+    ones = torch.ones((2, nt, nt), dtype=torch.uint8, device="cuda")
+    assert torch.equal(_attend(g["q"], store, 256).view(torch.int16),
+                       _attend(g["q"], store, 256, mask=ones).view(torch.int16))
+    rng = np.random.default_rng(9)
+    mask = (rng.random((2, nt, nt)) < 0.3).astype(np.uint8)
+    mask[:, 2, :] = 0
+    out = _attend(g["q"], store, 256, mask=torch.from_numpy(mask).cuda(), sol=True)
+
+    def sol_ref(h, rows, q, kc, ks, vc, vs):
+        return oracle.kvi8r_sol_attention(q, kc, ks, vc, vs, SCALE, rows, mask[h])
+    _check_rows(lambda h: bits["q"][:, h], store, out, range(2), lambda h: np.arange(w.seq), "sol32", sol_ref)
+
+
+def test_finer_scales_land_closer_to_unquantised_attention():
+    # outlier keys (4 channels x20): the per-row scale is set by the outliers' groups
+    w = synth.WORKLOADS["outlier16k"]
+    g = gpu_inputs(w)
+    bits_q = lambda h: synth.head_bf16(w, "q", h)
+    s32 = _store32(g["k"], g["v"])
+    out32 = _attend(g["q"], s32, 4096)
+    kc, vc, sc = h3a.new_kvi8r_store(w.seq, w.heads)
+    h3a.h3a_kv_quantize(g["k"], kc, sc[0])
+    h3a.h3a_kv_quantize(g["v"], vc, sc[1])
+    out8 = torch.empty_like(g["q"])
+    h3a.h3a_attention(g["q"], kc, vc, sc, out8, q_chunk=4096, mode="kvi8r")
+    torch.cuda.synchronize()
+    g32, g8, ref_all = [], [], []
+    for h in (0, 3, 5, 7):
+        rows = synth.sampled_rows(w, h, 256)
+        ref_all.append(oracle.exact_attention_bf16(bits_q(h)[rows], synth.head_bf16(w, "k", h),
+                                                   synth.head_bf16(w, "v", h), SCALE))
+        idx = torch.from_numpy(rows).cuda()
+        g32.append(oracle.bf16_to_f64(host_u16(out32[idx, h])))
+        g8.append(oracle.bf16_to_f64(host_u16(out8[idx, h])))
+    ref = np.concatenate(ref_all)
+    e32, e8 = rel_l2(np.concatenate(g32), ref), rel_l2(np.concatenate(g8), ref)
+    say("against unquantised attention: kvi8r32", e32, "kvi8r", e8)
+    assert e32 < e8
