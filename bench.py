@@ -7,8 +7,12 @@ One step = one pass of the whole path over one batch of synthetic input at
   2. kvi8r attention: h3a_attention (rotate each query chunk, attention over the
      int8 store dequantised in the loop, un-rotate once);
   3. exact attention: h3a_attention on the bf16 store.
-Inputs are resident in HBM before timing.  `value` is the algorithmic attention
-throughput of the step, 2 x 4*S*S*H*128 flop over the step's wall time.
+Inputs are resident in HBM before timing.  After the timed steps, extra legs
+(each its own JSON object) time the per-row routed call (exact_av_rows) and
+the per-32-value store (kvi8r32) at long217k, and the hard and Sol arms of the
+block-sparse path at sparse64k.
+`value` is the algorithmic attention throughput of the step,
+2 x 4*S*S*H*128 flop over the step's wall time.
 
 Prints one JSON line.  Only one GPU is supported; --gpus N with N > 1 exits.
 """
@@ -185,6 +189,67 @@ def sparse_legs(h3a, dev, reps: int):
     return res
 
 
+def routed_leg(h3a, w, x, store, kvi8r_ms: float, ws, stream, reps: int = 2):
+    """h3a_attention_routed at long217k: a 5760-row text prefix and a 2240-row audio tail (3.7 % of the
+    rows, the text + audio share the node page gives) attend the bf16 K/V exactly, the rest the kvi8r store."""
+    import torch
+
+    spans = [(0, 5760), (w.seq - 2240, w.seq)]
+    out = torch.empty_like(x["q"])
+    call = lambda: h3a.h3a_attention_routed(x["q"], x["k"], x["v"], store, out, exact_spans=spans,
+                                            q_chunk=w.q_chunk, kv_block=w.kv_block, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = attention_flops(w)
+    return {"workload": w.name, "exact_spans": spans, "exact_row_frac": round(8000 / w.seq, 4),
+            "ms": round(ms, 3), "tflops": round(flops / (ms / 1000) / 1e12, 2),
+            "ms_vs_kvi8r": round(ms - kvi8r_ms, 3)}
+
+
+def kvi8r32_leg(h3a, w, x, ws, stream, reps: int = 2):
+    """The per-32-value store (kvi8r32) at long217k: build (h3a_kv_quantize_g32 per kv_chunk) and attention."""
+    import torch
+
+    kc, vc, sc = h3a.new_kvi8r_store(w.seq, w.heads, device=x["q"].device, per32=True)
+    out = torch.empty_like(x["q"])
+
+    def build():
+        for t0 in range(0, w.seq, w.q_chunk):
+            h3a.h3a_kv_quantize(x["k"][t0:t0 + w.q_chunk], kc, sc[0], token_offset=t0)
+            h3a.h3a_kv_quantize(x["v"][t0:t0 + w.q_chunk], vc, sc[1], token_offset=t0)
+
+    attend = lambda: h3a.h3a_attention(x["q"], kc, vc, sc, out, q_chunk=w.q_chunk, kv_block=w.kv_block,
+                                       mode="kvi8r32", workspace=ws)
+    build()
+    attend()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    q_ms = a_ms = 0.0
+    for _ in range(reps):
+        ev[0].record(stream)
+        build()
+        ev[1].record(stream)
+        attend()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        q_ms += ev[0].elapsed_time(ev[1])
+        a_ms += ev[1].elapsed_time(ev[2])
+    q_ms, a_ms = q_ms / reps, a_ms / reps
+    flops = attention_flops(w)
+    store_bytes = 2.0 * w.seq * w.heads * (256 + 128 + 8)  # per tensor row: bf16 in, int8 codes + 4 fp16 scales out
+    return {"workload": w.name, "mode": "kvi8r32", "quant_ms": round(q_ms, 3),
+            "quant_GB_per_s": round(store_bytes / (q_ms / 1000) / 1e9, 1), "attention_ms": round(a_ms, 3),
+            "tflops": round(flops / (a_ms / 1000) / 1e12, 2),
+            "frac_of_peak": round(flops / (a_ms / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +262,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run one plain 1 GiB device-to-device copy (a known-size "
                          "reference for HBM traffic counters)")
+    ap.add_argument("--no-routed", action="store_true", help="skip the per-row routed (exact_av_rows) leg")
+    ap.add_argument("--no-kvi8r32", action="store_true", help="skip the per-32-value store (kvi8r32) leg")
     ap.add_argument("--sparse-only", action="store_true",
                     help="run only the block-sparse legs and print their JSON (for profiling the sparse kernels)")
     args = ap.parse_args()
@@ -326,9 +393,18 @@ def main() -> int:
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 1 << 30
         del src, dst
+    if not args.no_routed:
+        log("routed leg ...")
+        res["long217k_routed"] = routed_leg(h3a, w, x, (kc, vc, sc), per["kvi8r"], ws, stream)
+        log(f"routed: {res['long217k_routed']['ms']} ms ({res['long217k_routed']['ms_vs_kvi8r']:+.1f} ms vs kvi8r)")
+    if not args.no_kvi8r32:
+        log("kvi8r32 leg ...")
+        del out_r
+        res["long217k_kvi8r32"] = kvi8r32_leg(h3a, w, x, ws, stream)
+        log(f"kvi8r32: attention {res['long217k_kvi8r32']['tflops']} TFLOP/s")
     if not args.no_sparse:
         log("sparse64k leg ...")
-        del x, out_r, out_e, ws
+        del x, out_e, ws
         torch.cuda.empty_cache()
         res.update(sparse_legs(h3a, dev, reps=3))
         log(f"sparse64k: hard {res['sparse64k']['tflops']} TFLOP/s, sol {res['sparse64k_sol']['tflops']} TFLOP/s")
