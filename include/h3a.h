@@ -14,8 +14,9 @@
  *
  * Conventions shared by every call
  *   - Every tensor pointer is device memory owned by the caller, and must stay
- *     valid until the work queued on `stream` has finished (the one host
- *     array, h3a_attention_routed's exact_spans, is read during the call).  The library keeps
+ *     valid until the work queued on `stream` has finished.  Exceptions:
+ *     h3a_attention_routed's exact_spans (host memory, read during the call)
+ *     and h3a_attention_host_kv's store (pinned host memory).  The library keeps
  *     no pointer after a call returns and allocates no device memory; scratch
  *     space comes only through the `workspace` argument.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
@@ -200,6 +201,44 @@ int32_t h3a_attention_routed(const void* q, const void* k_bf16, const void* v_bf
                              int32_t head_dim, float softmax_scale, int64_t q_chunk, int64_t kv_block,
                              const int64_t* exact_spans, int32_t n_spans, void* out, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/*
+ * h3a_attention_host_kv_workspace_bytes -- device workspace of
+ * h3a_attention_host_kv.  Returns 0 when none is needed or the arguments are
+ * invalid.
+ */
+size_t h3a_attention_host_kv_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim,
+                                             int64_t q_chunk, int64_t kv_block, int32_t mode);
+
+/*
+ * h3a_attention_host_kv -- h3a_attention (dense, no tile_mask) with the K/V
+ * store in pinned host memory, brought to the GPU one kv_block at a time
+ * [P1 Inputs table, kv_block row: K/V attended in blocks with a log-sum-exp
+ * combine, kept for a host-staged K/V store].
+ *
+ * For every query chunk, the store is copied block by block (kv_block tokens,
+ * 0 = 16384) into one of two device buffers in the workspace, on a copy
+ * stream of the library's own, while the previous block is attended on
+ * `stream`.  Each block's launch resumes every query row's running max, row
+ * sum and output accumulators from the workspace and leaves them there for
+ * the next block; the last block writes the output.  The output is bitwise the
+ * one h3a_attention gives for the same store resident on the GPU.
+ *
+ * k_host, v_host, scales_host: the store of `mode` (as for h3a_attention) in
+ *              PINNED host memory (hipHostMalloc), 16-byte aligned; pageable
+ *              memory is H3A_EINVAL.  Must stay valid and unchanged until the
+ *              work queued on `stream` has finished.
+ * q, out:      device memory, as for h3a_attention.
+ * workspace:   h3a_attention_host_kv_workspace_bytes(...) bytes of device
+ *              memory (two K/V blocks, one query chunk's state).
+ * The copy stream waits for the work queued on `stream` before the call, and
+ * `stream` waits for every copy it uses, so the call is ordered on `stream`
+ * like any other.
+ */
+int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_host, const void* scales_host,
+                              int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                              int64_t q_chunk, int64_t kv_block, int32_t mode, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * h3a_rotate_rows -- y = fp16(x H) for n_rows rows of 128 bf16 values (the

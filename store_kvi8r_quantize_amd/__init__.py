@@ -8,7 +8,8 @@ There is no CPU fallback: if the library is not built, or its ABI version does
 not match, every call raises.
 
 Functions carry the C names: h3a_kv_quantize (+ h3a_kv_quantize_g32, chosen by the
-scales' shape), h3a_attention, h3a_attention_routed,
+scales' shape), h3a_attention, h3a_attention_routed, h3a_attention_host_kv
+(+ its workspace query),
 h3a_attention_workspace_bytes, h3a_rotate_rows, h3a_unrotate_rows,
 h3a_timing_enable, h3a_timing_collect, h3a_abi_version.
 """
@@ -68,6 +69,10 @@ def _load():
     lib.h3a_attention_routed.restype = i32
     lib.h3a_attention_routed.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64,
                                          ctypes.POINTER(ctypes.c_int64), i32, vp, vp, sz, vp]
+    lib.h3a_attention_host_kv_workspace_bytes.restype = sz
+    lib.h3a_attention_host_kv_workspace_bytes.argtypes = [i64, i64, i32, i32, i64, i64, i32]
+    lib.h3a_attention_host_kv.restype = i32
+    lib.h3a_attention_host_kv.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64, i32, vp, vp, sz, vp]
     lib.h3a_rotate_rows.restype = i32
     lib.h3a_rotate_rows.argtypes = [vp, vp, i64, vp]
     lib.h3a_unrotate_rows.restype = i32
@@ -240,6 +245,46 @@ def h3a_attention_routed(q, k_bf16, v_bf16, store, out, *, exact_spans, q_chunk:
     _check(lib.h3a_attention_routed(_ptr(q), _ptr(k_bf16), _ptr(v_bf16), _ptr(kc), _ptr(vc), _ptr(sc), s_q, s_kv,
                                     n_heads, head_dim, float(softmax_scale), int(q_chunk), int(kv_block), spans,
                                     len(flat) // 2, _ptr(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
+    return out
+
+
+def h3a_attention_host_kv_workspace_bytes(s_q: int, s_kv: int, n_heads: int, q_chunk: int, kv_block: int, mode,
+                                          head_dim: int = HEAD_DIM) -> int:
+    mode = MODES.get(mode, mode)
+    return int(_load().h3a_attention_host_kv_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, kv_block,
+                                                             int(mode)))
+
+
+def h3a_attention_host_kv(q, k_host, v_host, scales_host, out, *, q_chunk: int, kv_block: int = 0, mode="kvi8r",
+                          softmax_scale: float | None = None, workspace=None, stream=None):
+    """h3a_attention with the K/V store in pinned host memory (CPU tensors with pin_memory), streamed to the GPU
+    one kv_block at a time.  Store layouts as for h3a_attention; q and out are GPU tensors."""
+    lib = _load()
+    mode = MODES.get(mode, mode)
+    _need(q, "q", torch.bfloat16)
+    _need(out, "out", torch.bfloat16)
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be contiguous [s_q, n_heads, head_dim] tensors of equal shape")
+    want = torch.bfloat16 if mode == MODE_EXACT_BF16 else torch.int8
+    for name, t in (("k_host", k_host), ("v_host", v_host), ("scales_host", scales_host)):
+        if t is None:
+            continue
+        if t.device.type != "cpu" or not t.is_pinned() or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous pinned CPU tensor")
+    if k_host.dtype != want or v_host.dtype != want:
+        raise ValueError(f"k_host / v_host must be {want} for mode {mode}")
+    s_q, n_heads, head_dim = q.shape
+    s_kv = k_host.shape[0] if mode == MODE_EXACT_BF16 else k_host.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    need = int(lib.h3a_attention_host_kv_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, kv_block, int(mode)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    hp = lambda t: None if t is None else t.data_ptr()
+    _check(lib.h3a_attention_host_kv(_ptr(q), hp(k_host), hp(v_host), hp(scales_host), s_q, s_kv, n_heads, head_dim,
+                                     float(softmax_scale), int(q_chunk), int(kv_block), int(mode), _ptr(out),
+                                     _ptr(workspace), ws_bytes, _stream(q, stream)))
     return out
 
 

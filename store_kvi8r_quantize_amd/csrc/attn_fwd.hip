@@ -689,7 +689,15 @@ void attn_fwd_sparse_sol_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt, SolArgs
 // the shorter chain of dependent work), so group 1 starts its softmax right
 // after the barrier.  Tiles are triple-buffered in LDS: during period i tiles
 // i-1 and i are read while tile i+1 is written.
-template <int MODE>
+// STATE: the K/V is one block of a longer store ("H3 Streamed Blocks" node
+// page, kv_block row: K/V attended block by block with a log-sum-exp combine).
+// Each thread resumes its rows' running max, row sum and O accumulators from
+// a.state_in (unless null) and leaves them in a.state_out (unless null, in
+// which case it writes the normalised output).  The layout is one array per
+// register, indexed by the thread's position in the grid, so the state moves
+// in coalesced 256-byte runs.  Carrying it through memory is exact, so a store
+// attended block by block gives the bits of one pass over the whole store.
+template <int MODE, bool STATE = false>
 __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
   constexpr int NS = 256;  // staging threads (group 0)
   constexpr int BM = 256;
@@ -721,6 +729,19 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
   for (int i = 0; i < 4; ++i) rb.acc[i] = f32x16{};
   rb.m = -__builtin_inff();
   rb.l = 0.0f;
+  const int64_t state_stride = (int64_t)gridDim.x * 512;      // one array per state register
+  const int64_t state_at = (int64_t)b * 512 + tid;             // this thread's slot (logical block b)
+  if constexpr (STATE) {
+    if (a.state_in != nullptr) {
+      const float* sp = a.state_in + state_at;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) rb.acc[i][j] = sp[(16 * i + j) * state_stride];
+      rb.m = sp[64 * state_stride];
+      rb.l = sp[65 * state_stride];
+    }
+  }
 
   const int n = n_kt;
   const float sl2 = a.scale_log2;
@@ -795,6 +816,18 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
       pv_block<MODE>(rb, lv(n - 1));
     }
     __syncthreads();
+  }
+  if constexpr (STATE) {
+    if (a.state_out != nullptr) {
+      float* sp = a.state_out + state_at;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sp[(16 * i + j) * state_stride] = rb.acc[i][j];
+      sp[64 * state_stride] = rb.m;
+      sp[65 * state_stride] = rb.l;
+      return;
+    }
   }
   store_rows<MODE>(rb, a, head, g);
 }
@@ -912,6 +945,26 @@ hipError_t launch_dense(const AttnChunk& a, hipStream_t stream) {
   if (n_wg == 0) return hipSuccess;
   hipLaunchKernelGGL((attn_fwd_dense_kernel<MODE>), dim3((unsigned)n_wg), dim3(512), 0, stream, a, n_qt, n_kt);
   return hipGetLastError();
+}
+
+int64_t dense_state_floats(int64_t rows, int32_t n_heads) {
+  return (rows + 255) / 256 * n_heads * 512 * (int64_t)kStateFloats;
+}
+
+template <int MODE>
+hipError_t launch_dense_block(const AttnChunk& a, hipStream_t stream) {
+  const int32_t n_qt = (int32_t)((a.rows + 255) / 256);
+  const int32_t n_kt = (int32_t)((a.s_kv + kTile - 1) / kTile);
+  const int64_t n_wg = (int64_t)n_qt * a.n_heads;
+  if (n_wg == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_dense_kernel<MODE, true>), dim3((unsigned)n_wg), dim3(512), 0, stream, a, n_qt, n_kt);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_block(int mode, const AttnChunk& a, hipStream_t stream) {
+  if (mode == 0) return launch_dense_block<0>(a, stream);
+  if (mode == 1) return launch_dense_block<1>(a, stream);
+  return launch_dense_block<2>(a, stream);
 }
 
 hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, const SolArgs* sol, hipStream_t stream) {

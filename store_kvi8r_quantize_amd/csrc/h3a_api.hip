@@ -172,6 +172,94 @@ int check_workspace(const void* workspace, size_t workspace_bytes, const Workspa
   return check_buffer(workspace, wl.total, 256, "workspace");
 }
 
+// `p` must be pinned host memory (hipHostMalloc) with `bytes` bytes inside one allocation.
+int check_host_buffer(const void* p, uint64_t bytes, const char* name) {
+  if (bytes == 0) return H3A_OK;
+  if (p == nullptr) return fail(H3A_EINVAL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return fail(H3A_EINVAL, "%s is not 16-byte aligned", name);
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();
+    return fail(H3A_EINVAL, "%s is not pinned host memory (allocate it with hipHostMalloc)", name);
+  }
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(H3A_EINVAL, "%s: cannot query its allocation (%s)", name, hipGetErrorString(e));
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+  if (q < b || (q - b) + bytes > size)
+    return fail(H3A_EINVAL, "%s: needs %llu bytes but its allocation holds %llu from this pointer", name,
+                (unsigned long long)bytes, (unsigned long long)(q >= b ? size - (q - b) : 0));
+  return H3A_OK;
+}
+
+// Device workspace of h3a_attention_host_kv: the per-chunk buffers of a dense
+// call, the (m, l, O) state of one query chunk, and two K/V block buffers.
+struct StagedLayout {
+  WorkspaceLayout base;
+  uint64_t state = 0;
+  uint64_t blk[2] = {0, 0};  // each: K, V, K scales, V scales
+  uint64_t k_bytes = 0, s_bytes = 0;  // per block buffer: K (= V) bytes, K (= V) scale bytes
+  int64_t blk_rows = 0;
+  uint64_t total = 0;
+};
+
+int64_t default_kv_block(int64_t kv_block) { return kv_block > 0 ? kv_block : 16384; }
+
+bool staged_layout(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chunk, int64_t kv_block, int32_t mode,
+                   StagedLayout* w) {
+  *w = StagedLayout{};
+  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, false, false, &w->base)) return false;
+  if (s_q <= 0 || s_kv <= 0) {
+    w->total = w->base.total;
+    return true;
+  }
+  const int64_t rows = q_chunk < s_q ? q_chunk : s_q;
+  const int64_t blk = default_kv_block(kv_block) < s_kv ? default_kv_block(kv_block) : s_kv;
+  const int64_t g = mode == H3A_MODE_KVI8R32 ? 4 : 1;
+  int64_t kb;
+  if (!mul_ok(blk * n_heads, (int64_t)H3A_HEAD_DIM * (mode == H3A_MODE_EXACT_BF16 ? 2 : 1), &kb)) return false;
+  const int64_t st = h3a::dense_state_floats(rows, n_heads) * 4;
+  uint64_t off = w->base.total;
+  w->state = off;
+  off = align256(off + (uint64_t)st);
+  w->k_bytes = align256((uint64_t)kb);
+  w->s_bytes = mode == H3A_MODE_EXACT_BF16 ? 0 : align256((uint64_t)(blk * n_heads * g * 2));
+  for (int i = 0; i < 2; ++i) {
+    w->blk[i] = off;
+    off += 2 * w->k_bytes + 2 * w->s_bytes;
+  }
+  w->blk_rows = blk;
+  w->total = off;
+  return true;
+}
+
+// One copy stream per device for host-staged K/V (default priority, does not
+// synchronise with the null stream).  Kept until the process ends.
+std::mutex g_copy_mu;
+std::vector<std::pair<int, hipStream_t>> g_copy_streams;
+
+hipError_t copy_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_copy_mu);
+  for (auto& p : g_copy_streams)
+    if (p.first == dev) {
+      *out = p.second;
+      return hipSuccess;
+    }
+  hipStream_t s = nullptr;
+  if ((e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking)) != hipSuccess) return e;
+  g_copy_streams.emplace_back(dev, s);
+  *out = s;
+  return hipSuccess;
+}
+
 // ---- the query-chunk loop -----------------------------------------------------------
 // One validated call over one store.
 struct Pass {
@@ -447,6 +535,151 @@ int32_t h3a_attention_routed(const void* q, const void* k_bf16, const void* v_bf
     r = e;
   }
   return H3A_OK;
+}
+
+size_t h3a_attention_host_kv_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim,
+                                             int64_t q_chunk, int64_t kv_block, int32_t mode) {
+  if (head_dim != H3A_HEAD_DIM || n_heads < 1 || s_kv < 0 || kv_block < 0 || kv_block % H3A_TILE != 0) return 0;
+  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32) return 0;
+  StagedLayout w;
+  if (!staged_layout(s_q, s_kv, n_heads, q_chunk, kv_block, mode, &w)) return 0;
+  return (size_t)w.total;
+}
+
+int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_host, const void* scales_host,
+                              int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                              int64_t q_chunk, int64_t kv_block, int32_t mode, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32)
+    return fail(H3A_EINVAL, "unknown mode %d", mode);
+  int rc;
+  if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
+  if (mode != H3A_MODE_EXACT_BF16 && scales_host == nullptr && s_kv > 0)
+    return fail(H3A_EINVAL, "kvi8r modes need scales");
+  if (mode == H3A_MODE_EXACT_BF16 && scales_host != nullptr) return fail(H3A_EINVAL, "exact mode takes no scales");
+  if (s_q == 0) return H3A_OK;
+  if ((rc = check_rows(q, out, s_q, n_heads)) != H3A_OK) return rc;
+  const int64_t g = mode == H3A_MODE_KVI8R32 ? 4 : 1;
+  int64_t n_kv;
+  if (!mul_ok(s_kv, (int64_t)n_heads * H3A_HEAD_DIM, &n_kv)) return fail(H3A_EINVAL, "size overflow");
+  const uint64_t kv_bytes = (uint64_t)n_kv * (mode == H3A_MODE_EXACT_BF16 ? 2 : 1);
+  if ((rc = check_host_buffer(k_host, kv_bytes, "k_host")) != H3A_OK) return rc;
+  if ((rc = check_host_buffer(v_host, kv_bytes, "v_host")) != H3A_OK) return rc;
+  if (mode != H3A_MODE_EXACT_BF16 &&
+      (rc = check_host_buffer(scales_host, (uint64_t)s_kv * n_heads * g * 4, "scales_host")) != H3A_OK)
+    return rc;
+  StagedLayout wl;
+  if (!staged_layout(s_q, s_kv, n_heads, q_chunk, kv_block, mode, &wl)) return fail(H3A_EINVAL, "size overflow");
+  if (wl.total > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.total)
+      return fail(H3A_EWORKSPACE, "workspace needs %llu bytes (got %llu)", (unsigned long long)wl.total,
+                  (unsigned long long)(workspace == nullptr ? 0 : workspace_bytes));
+    if ((rc = check_buffer(workspace, wl.total, 256, "workspace")) != H3A_OK) return rc;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  Pass p = make_pass(mode, q, out, nullptr, nullptr, nullptr, s_q, s_kv, n_heads, softmax_scale, q_chunk, ws,
+                     wl.base, stream);
+  if (s_kv == 0) return attend_rows(p, 0, s_q);  // no K/V: every row is zero
+
+  hipStream_t cs;
+  hipError_t e;
+  if ((e = copy_stream(&cs)) != hipSuccess) return hip_fail(e, "copy stream");
+  // ready: the caller's earlier work on `stream` (which may still use the workspace);
+  // copied[i] / freed[i]: block buffer i filled / released by its kernel.
+  hipEvent_t ready = nullptr, copied[2] = {nullptr, nullptr}, freed[2] = {nullptr, nullptr};
+  auto destroy = [&]() {
+    for (hipEvent_t ev : {ready, copied[0], copied[1], freed[0], freed[1]})
+      if (ev) (void)hipEventDestroy(ev);
+  };
+  for (hipEvent_t* ev : {&ready, &copied[0], &copied[1], &freed[0], &freed[1]})
+    if ((e = hipEventCreateWithFlags(ev, hipEventDisableTiming)) != hipSuccess) {
+      destroy();
+      return hip_fail(e, "hipEventCreate");
+    }
+  int status = H3A_OK;
+  auto check = [&](hipError_t err, const char* what) {
+    if (err != hipSuccess && status == H3A_OK) status = hip_fail(err, what);
+    return status == H3A_OK;
+  };
+  if (check(hipEventRecord(ready, p.st), "hipEventRecord")) check(hipStreamWaitEvent(cs, ready, 0), "wait");
+
+  const char* kh = static_cast<const char*>(k_host);
+  const char* vh = static_cast<const char*>(v_host);
+  const char* sh = static_cast<const char*>(scales_host);
+  float* state = reinterpret_cast<float*>(ws + wl.state);
+  const int64_t blk = wl.blk_rows, n_blk = (s_kv + blk - 1) / blk;
+  int64_t k = 0;  // blocks streamed so far in this call
+  for (int64_t c0 = 0; c0 < s_q && status == H3A_OK; c0 += q_chunk) {
+    const int64_t rows = (s_q - c0) < q_chunk ? (s_q - c0) : q_chunk;
+    const int64_t off = c0 * n_heads * H3A_HEAD_DIM;
+    h3a::AttnChunk a{};
+    a.rows = rows;
+    a.n_heads = n_heads;
+    a.scale_log2 = p.scale_log2;
+    if (mode != H3A_MODE_EXACT_BF16) {
+      uint16_t* qrot = reinterpret_cast<uint16_t*>(ws + wl.base.qrot);
+      if (!check(h3a::launch_rotate_q(p.q + off, qrot, rows * n_heads, p.st), "rotate_q launch")) break;
+      a.q = qrot;
+      a.out = ws + wl.base.orot;
+    } else {
+      a.q = p.q + off;
+      a.out = p.out + off;
+    }
+    for (int64_t j = 0; j < n_blk && status == H3A_OK; ++j, ++k) {
+      const int slot = (int)(k & 1);
+      const int64_t t0 = j * blk, bl = (s_kv - t0) < blk ? (s_kv - t0) : blk;
+      char* bk = ws + wl.blk[slot];
+      char* bv = bk + wl.k_bytes;
+      char* bks = bv + wl.k_bytes;
+      char* bvs = bks + wl.s_bytes;
+      if (k >= 2 && !check(hipStreamWaitEvent(cs, freed[slot], 0), "wait")) break;
+      if (mode == H3A_MODE_EXACT_BF16) {  // token-major: a block is one contiguous range
+        const size_t nb = (size_t)bl * n_heads * H3A_HEAD_DIM * 2, o = (size_t)t0 * n_heads * H3A_HEAD_DIM * 2;
+        check(hipMemcpyAsync(bk, kh + o, nb, hipMemcpyHostToDevice, cs), "K block copy");
+        check(hipMemcpyAsync(bv, vh + o, nb, hipMemcpyHostToDevice, cs), "V block copy");
+      } else {  // head-major: one strided row of bl tokens per head
+        const size_t w = (size_t)bl * H3A_HEAD_DIM, sp = (size_t)s_kv * H3A_HEAD_DIM, o = (size_t)t0 * H3A_HEAD_DIM;
+        check(hipMemcpy2DAsync(bk, w, kh + o, sp, w, n_heads, hipMemcpyHostToDevice, cs), "K block copy");
+        check(hipMemcpy2DAsync(bv, w, vh + o, sp, w, n_heads, hipMemcpyHostToDevice, cs), "V block copy");
+        const size_t ws2 = (size_t)bl * g * 2, ss = (size_t)s_kv * g * 2, so = (size_t)t0 * g * 2;
+        const size_t vso = (size_t)s_kv * n_heads * g * 2;  // V scales follow the K scales
+        check(hipMemcpy2DAsync(bks, ws2, sh + so, ss, ws2, n_heads, hipMemcpyHostToDevice, cs), "K scale copy");
+        check(hipMemcpy2DAsync(bvs, ws2, sh + vso + so, ss, ws2, n_heads, hipMemcpyHostToDevice, cs),
+              "V scale copy");
+      }
+      if (!check(hipEventRecord(copied[slot], cs), "hipEventRecord")) break;
+      if (!check(hipStreamWaitEvent(p.st, copied[slot], 0), "wait")) break;
+      a.k = bk;
+      a.v = bv;
+      a.k_scale = reinterpret_cast<const uint16_t*>(bks);
+      a.v_scale = reinterpret_cast<const uint16_t*>(bvs);
+      a.s_kv = bl;
+      a.state_in = j == 0 ? nullptr : state;
+      a.state_out = j + 1 == n_blk ? nullptr : state;
+      hipEvent_t ev0 = nullptr, ev1 = nullptr;
+      if (p.timing) {
+        if (!check(hipEventCreate(&ev0), "hipEventCreate") || !check(hipEventCreate(&ev1), "hipEventCreate") ||
+            !check(hipEventRecord(ev0, p.st), "hipEventRecord"))
+          break;
+      }
+      if (!check(h3a::launch_attn_fwd_block(mode, a, p.st), "attn_fwd launch")) break;
+      if (p.timing) {
+        if (!check(hipEventRecord(ev1, p.st), "hipEventRecord")) break;
+        std::lock_guard<std::mutex> lk(g_timing_mu);
+        g_events.emplace_back(ev0, ev1);
+      }
+      if (!check(hipEventRecord(freed[slot], p.st), "hipEventRecord")) break;
+    }
+    if (status == H3A_OK && mode != H3A_MODE_EXACT_BF16)
+      check(h3a::launch_unrotate_o(reinterpret_cast<const float*>(ws + wl.base.orot), p.out + off, rows * n_heads,
+                                   p.st),
+            "unrotate_o launch");
+  }
+  destroy();
+  return status;
 }
 
 int32_t h3a_rotate_rows(const void* x_bf16, void* y_f16, int64_t n_rows, void* stream) {

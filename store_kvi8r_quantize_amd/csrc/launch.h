@@ -24,8 +24,14 @@ struct AttnChunk {
   const uint16_t* k_scale; // kvi8r: fp16 [H, s_kv]; kvi8r32: fp16 [H, s_kv, 4]
   const uint16_t* v_scale;
   void* out;               // exact: bf16 [rows, H, 128]; kvi8r: fp32 O' (normalised, rotated) [rows, H, 128]
-  const int32_t* counts;   // sparse: kept-tile count per (head, 64-row q-tile) of the chunk
-  const int32_t* lists;    // sparse: kept KV-tile indices [H, n_qtiles, n_kt], increasing
+  union {
+    const int32_t* counts;  // sparse: kept-tile count per (head, 64-row q-tile) of the chunk
+    const float* state_in;  // dense, K/V streamed block by block: (m, l, O) to resume from; null on the first block
+  };
+  union {
+    const int32_t* lists;   // sparse: kept KV-tile indices [H, n_qtiles, n_kt], increasing
+    float* state_out;       // dense, block by block: where to leave (m, l, O); null on the last block
+  };
   int64_t rows;
   int64_t s_kv;
   int32_t n_heads;
@@ -48,6 +54,13 @@ constexpr int kSparseBlockRows = 64;  // q-tile of the sparse kernel = the routi
 
 // sol: null, or the Sol residual (sparse only).
 hipError_t launch_attn_fwd(int mode, bool sparse, const AttnChunk& a, const SolArgs* sol, hipStream_t stream);
+
+// Dense attention of one query chunk against one K/V block, carrying the
+// online-softmax state through a.state_in / a.state_out.  The state takes
+// kStateFloats floats per thread of the launch: dense_state_floats(rows, H).
+constexpr int kStateFloats = 66;  // 64 O accumulators, m, l
+int64_t dense_state_floats(int64_t rows, int32_t n_heads);
+hipError_t launch_attn_fwd_block(int mode, const AttnChunk& a, hipStream_t stream);
 
 // Kept-tile lists (and, when drops is not null, dropped-tile lists) for the
 // q-tiles [qt0, qt0 + n_qt) of every head.

@@ -141,6 +141,35 @@ def test_quantize_g32_rejects_bad_arguments(lib):
     assert lib.h3a_kv_quantize_g32(None, 256, 0, 2, 128, 0, 0, None, None, None) == 0
 
 
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(head_dim=64), -2, "head_dim"),
+    (dict(mode=3), -1, "mode"),
+    (dict(mode=1, scales=None), -1, "scales"),
+    (dict(mode=0, scales=16), -1, "no scales"),
+    (dict(kv_block=100), -1, "kv_block"),
+    (dict(q_chunk=0), -1, "q_chunk"),
+])
+def test_host_kv_rejects_bad_arguments(lib, kw, status, msg):
+    a = dict(s_q=1024, s_kv=1024, n_heads=2, head_dim=128, scale=0.088, q_chunk=256, kv_block=256, mode=1, scales=16)
+    a.update(kw)
+    rc = lib.h3a_attention_host_kv(None, None, None, a["scales"], a["s_q"], a["s_kv"], a["n_heads"], a["head_dim"],
+                                   a["scale"], a["q_chunk"], a["kv_block"], a["mode"], None, None, 0, None)
+    assert rc == status
+    assert msg in lib.h3a_last_error().decode()
+
+
+def test_host_kv_workspace_sizes():
+    dense = h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, "kvi8r", False)
+    staged = h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 256, "kvi8r")
+    state = 1 * 2 * 512 * 66 * 4                      # one query chunk of 256 rows, 2 heads
+    blocks = 2 * (2 * 256 * 2 * 128 + 2 * 256 * 2 * 2)  # two buffers: K, V codes + their scales for 256 tokens
+    assert staged >= dense + state + blocks
+    assert h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 100, "kvi8r") == 0
+    # kv_block 0 = 16384, clipped to the store
+    assert h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 0, "exact") == \
+        h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 1024, "exact")
+
+
 def test_workspace_sizes(lib):
     # kvi8r: rotated Q (fp16) + rotated output (fp32) for one chunk of rows
     assert h3a.h3a_attention_workspace_bytes(1024, 1024, 2, 256, "kvi8r", False) == 256 * 2 * 128 * 6
