@@ -8,8 +8,9 @@ One step = one pass of the whole path over one batch of synthetic input at
      int8 store dequantised in the loop, un-rotate once);
   3. exact attention: h3a_attention on the bf16 store.
 Inputs are resident in HBM before timing.  After the timed steps, extra legs
-(each its own JSON object) time the per-row routed call (exact_av_rows) and
-the per-32-value store (kvi8r32) at long217k, and the hard and Sol arms of the
+(each its own JSON object) time the per-row routed call (exact_av_rows), the
+host-staged K/V call (store in pinned host memory, PCIe-inclusive) and the
+per-32-value store (kvi8r32) at long217k, and the hard and Sol arms of the
 block-sparse path at sparse64k.
 `value` is the algorithmic attention throughput of the step,
 2 x 4*S*S*H*128 flop over the step's wall time.
@@ -250,6 +251,44 @@ def kvi8r32_leg(h3a, w, x, ws, stream, reps: int = 2):
             "frac_of_peak": round(flops / (a_ms / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4)}
 
 
+def host_kv_leg(h3a, w, x, store, dev_ms: dict, stream, reps: int = 1):
+    """h3a_attention_host_kv at long217k: the kvi8r and exact stores in pinned host memory, streamed one
+    kv_block at a time per query chunk.  Reports the time against the resident store and the PCIe bytes moved."""
+    import torch
+
+    res = {}
+    for mode in ("kvi8r", "exact"):
+        if mode == "kvi8r":
+            host = [torch.empty(t.shape, dtype=t.dtype, pin_memory=True).copy_(t) for t in store]
+            store_bytes = sum(t.numel() * t.element_size() for t in host)
+        else:
+            host = [torch.empty(x[t].shape, dtype=x[t].dtype, pin_memory=True).copy_(x[t]) for t in ("k", "v")]
+            host.append(None)
+            store_bytes = sum(t.numel() * t.element_size() for t in host[:2])
+        need = h3a.h3a_attention_host_kv_workspace_bytes(w.seq, w.seq, w.heads, w.q_chunk, w.kv_block, mode)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x["q"].device)
+        out = torch.empty_like(x["q"])
+        call = lambda: h3a.h3a_attention_host_kv(x["q"], *host, out, q_chunk=w.q_chunk, kv_block=w.kv_block,
+                                                 mode=mode, workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        n_chunks = -(-w.seq // w.q_chunk)
+        pcie = store_bytes * n_chunks
+        res[mode] = {"ms": round(ms, 3), "ms_resident": round(dev_ms[mode], 3),
+                     "tflops": round(attention_flops(w) / (ms / 1000) / 1e12, 2),
+                     "host_to_device_GB": round(pcie / 1e9, 2), "host_to_device_GB_per_s": round(pcie / ms / 1e6, 1),
+                     "device_workspace_GB": round(need / 1e9, 3), "resident_store_GB": round(store_bytes / 1e9, 3)}
+        del host, ws, out
+    return {"workload": w.name, "kv_block": w.kv_block, "q_chunk": w.q_chunk, **res}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +303,7 @@ def main() -> int:
                          "reference for HBM traffic counters)")
     ap.add_argument("--no-routed", action="store_true", help="skip the per-row routed (exact_av_rows) leg")
     ap.add_argument("--no-kvi8r32", action="store_true", help="skip the per-32-value store (kvi8r32) leg")
+    ap.add_argument("--no-host-kv", action="store_true", help="skip the host-staged K/V leg")
     ap.add_argument("--sparse-only", action="store_true",
                     help="run only the block-sparse legs and print their JSON (for profiling the sparse kernels)")
     args = ap.parse_args()
@@ -379,7 +419,7 @@ def main() -> int:
         },
         "kv_quantize": {"ms": round(per["quant"], 3), "GB_per_s": round(quant_bytes / (per["quant"] / 1000) / 1e9, 1),
                         "frac_of_hbm_peak": round(quant_bytes / (per["quant"] / 1000) / 1e9 / PEAK_HBM_GBPS, 4)},
-        "roofline": {"kernel": "attn_fwd_dense_kernel<1> (kvi8r, dense)", "bound": "mfma",
+        "roofline": {"kernel": "attn_fwd_dense_kernel<1, false> (kvi8r, dense)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": measured_traffic("kvi8r"),
                      "traffic_unit": "HBM bytes per launch (FETCH_SIZE x fetch factor + WRITE_SIZE x write factor)",
@@ -397,6 +437,11 @@ def main() -> int:
         log("routed leg ...")
         res["long217k_routed"] = routed_leg(h3a, w, x, (kc, vc, sc), per["kvi8r"], ws, stream)
         log(f"routed: {res['long217k_routed']['ms']} ms ({res['long217k_routed']['ms_vs_kvi8r']:+.1f} ms vs kvi8r)")
+    if not args.no_host_kv:
+        log("host-staged K/V leg ...")
+        res["long217k_host_kv"] = host_kv_leg(h3a, w, x, (kc, vc, sc), per, stream)
+        log(f"host-staged: kvi8r {res['long217k_host_kv']['kvi8r']['ms']} ms, "
+            f"exact {res['long217k_host_kv']['exact']['ms']} ms")
     if not args.no_kvi8r32:
         log("kvi8r32 leg ...")
         del out_r
