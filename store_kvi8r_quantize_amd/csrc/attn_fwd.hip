@@ -114,7 +114,7 @@ struct Stage {
   static constexpr int KU = 512 / NT;
   static constexpr int VU = 512 / NT;
   u32x4 k[KU][MODE == 0 ? 2 : 1];
-  uint32_t ks[KU];
+  uint32_t ks[MODE == 2 ? KU : 1];  // kvi8r32: each unit's group scale; kvi8r: key tid's scale (threads 0-63)
   uint32_t v[VU][4][MODE == 0 ? 2 : 1];
   uint32_t vs[VU][2];  // kvi8r: fp16 scales of the unit's 4 keys, packed in pairs
 };
@@ -146,9 +146,11 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
       const int u = tid + NT * j;
       st.k[j][0] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (u >> 3) * kHeadDim + 16 * (u & 7), 0, 0));
-      // kvi8r: the key's scale; kvi8r32: the scale of the unit's 32-value group (dims 16*(u&7)..)
-      st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, ((u >> 3) * G + (MODE == 2 ? (u & 7) >> 1 : 0)) * 2, 0, 0);
+      // kvi8r32: the scale of the unit's 32-value group (dims 16*(u&7)..)
+      if constexpr (MODE == 2) st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, ((u >> 3) * G + ((u & 7) >> 1)) * 2, 0, 0);
     }
+    if constexpr (MODE == 1)  // one scale per key: threads 0-63 (the first wave) fetch them
+      if (tid < kTile) st.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(rks, tid * 2, 0, 0);
   }
 }
 
@@ -242,7 +244,6 @@ __device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t
       const uint32_t u2 = w[2] ^ 0x80808080u, u3 = w[3] ^ 0x80808080u;
       c0 = u32x4{code_pair(u0, kSelLo), code_pair(u0, kSelHi), code_pair(u1, kSelLo), code_pair(u1, kSelHi)};
       c1 = u32x4{code_pair(u2, kSelLo), code_pair(u2, kSelHi), code_pair(u3, kSelLo), code_pair(u3, kSelHi)};
-      if (d16 == 0) lc[r] = (float)__builtin_bit_cast(_Float16, (uint16_t)st.ks[j]) * sl2;
     } else {  // kvi8r32: a key has four scales, so K is dequantised to fp16 here like V
       const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.ks[j]);
       const half2v s2 = {sc, sc};
@@ -257,6 +258,8 @@ __device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16) = c0;
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
   }
+  if constexpr (MODE == 1)
+    if (tid < kTile) lc[tid] = (float)__builtin_bit_cast(_Float16, (uint16_t)st.ks[0]) * sl2;
 }
 
 template <int MODE, int NT>
