@@ -111,10 +111,14 @@ def cpu_baseline(w, store, seconds: float):
     import oracle
     import synth
 
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        pools = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = max([i.get("num_threads", 1) for i in pools] or [1])
+        if pools:
+            blas = f"{pools[0].get('internal_api', '?')} {pools[0].get('version', '')}".strip()
     except Exception:  # threadpoolctl missing: report the affinity size
         cores = len(os.sched_getaffinity(0))
     kc, vc, sc = store
@@ -134,9 +138,11 @@ def cpu_baseline(w, store, seconds: float):
         if el >= seconds:
             break
     flops = 4.0 * rows * w.seq * 128
+    full = 4.0 * w.seq * w.seq * w.heads * 128  # one whole kvi8r attention pass
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"kvi8r attention (fp64 NumPy oracle) of {rows} query rows of head 0 against all "
-                      f"{w.seq} keys, in blocks of {block} rows, {el:.1f} s"}
+                      f"{w.seq} keys, in blocks of {block} rows, {el:.1f} s",
+            "blas": blas, "seconds_for_one_full_pass": round(full / (flops / el), 1)}
 
 
 def sparse_legs(h3a, dev, reps: int):
