@@ -126,6 +126,30 @@ std::mutex g_timing_mu;
 bool g_timing_on = false;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
 
+// A pair of timing events around one attention-kernel launch on `st`: begin()
+// records the start, end() the stop and hands both to the collection list;
+// a pair that never reached end() is destroyed with the guard.
+struct LaunchTimer {
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  hipError_t begin(hipStream_t st) {
+    hipError_t e;
+    if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess) return e;
+    return hipEventRecord(ev0, st);
+  }
+  hipError_t end(hipStream_t st) {
+    hipError_t e = hipEventRecord(ev1, st);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_events.emplace_back(ev0, ev1);
+    ev0 = ev1 = nullptr;
+    return hipSuccess;
+  }
+  ~LaunchTimer() {
+    if (ev0) (void)hipEventDestroy(ev0);
+    if (ev1) (void)hipEventDestroy(ev1);
+  }
+};
+
 // ---- argument checks shared by the attention entry points ----------------------
 int check_shapes(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chunk, int64_t kv_block,
                  float softmax_scale) {
@@ -291,7 +315,7 @@ Pass make_pass(int32_t mode, const void* q, void* out, const void* k, const void
   p.out = static_cast<uint16_t*>(out);
   p.k = k;
   p.v = v;
-  if (mode != H3A_MODE_EXACT_BF16) {
+  if (mode != H3A_MODE_EXACT_BF16 && scales != nullptr) {
     p.k_scale = static_cast<const uint16_t*>(scales);
     p.v_scale = p.k_scale + s_kv * n_heads * (mode == H3A_MODE_KVI8R32 ? 4 : 1);
   }
@@ -354,19 +378,11 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
                                        reinterpret_cast<int32_t*>(p.ws + p.wl.lists), drops, p.st)) != hipSuccess)
         return hip_fail(e, "route_build launch");
     }
-    hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    if (p.timing) {
-      if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess)
-        return hip_fail(e, "hipEventCreate");
-      if ((e = hipEventRecord(ev0, p.st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
+    LaunchTimer timer;
+    if (p.timing && (e = timer.begin(p.st)) != hipSuccess) return hip_fail(e, "timing event");
     if ((e = h3a::launch_attn_fwd(p.mode, sparse, a, p.sol ? &sa : nullptr, p.st)) != hipSuccess)
       return hip_fail(e, "attn_fwd launch");
-    if (p.timing) {
-      if ((e = hipEventRecord(ev1, p.st)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-      std::lock_guard<std::mutex> lk(g_timing_mu);
-      g_events.emplace_back(ev0, ev1);
-    }
+    if (p.timing && (e = timer.end(p.st)) != hipSuccess) return hip_fail(e, "timing event");
     if (p.mode != H3A_MODE_EXACT_BF16) {
       if ((e = h3a::launch_unrotate_o(reinterpret_cast<const float*>(p.ws + p.wl.orot), p.out + off,
                                       rows * p.n_heads, p.st)) != hipSuccess)
@@ -659,18 +675,10 @@ int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_h
       a.s_kv = bl;
       a.state_in = j == 0 ? nullptr : state;
       a.state_out = j + 1 == n_blk ? nullptr : state;
-      hipEvent_t ev0 = nullptr, ev1 = nullptr;
-      if (p.timing) {
-        if (!check(hipEventCreate(&ev0), "hipEventCreate") || !check(hipEventCreate(&ev1), "hipEventCreate") ||
-            !check(hipEventRecord(ev0, p.st), "hipEventRecord"))
-          break;
-      }
+      LaunchTimer timer;
+      if (p.timing && !check(timer.begin(p.st), "timing event")) break;
       if (!check(h3a::launch_attn_fwd_block(mode, a, p.st), "attn_fwd launch")) break;
-      if (p.timing) {
-        if (!check(hipEventRecord(ev1, p.st), "hipEventRecord")) break;
-        std::lock_guard<std::mutex> lk(g_timing_mu);
-        g_events.emplace_back(ev0, ev1);
-      }
+      if (p.timing && !check(timer.end(p.st), "timing event")) break;
       if (!check(hipEventRecord(freed[slot], p.st), "hipEventRecord")) break;
     }
     if (status == H3A_OK && mode != H3A_MODE_EXACT_BF16)
