@@ -611,19 +611,33 @@ __device__ __forceinline__ void attn_fwd_sparse_body(const AttnChunk& a, int32_t
   const uint16_t* lk = lds_k + c * kKStride + 8 * g;
   const uint16_t* lv = lds_v + c * kVStride + 4 * g;
 
+  // Kept-tile indices are the same in every lane: readfirstlane keeps the
+  // buffer descriptors built from them in scalar registers.
   Stage<MODE, NT> st;
-  if (n_tiles > 0) load_tile<MODE, NT>(st, a, head, list[0], tid);
+  if (n_tiles > 0) load_tile<MODE, NT>(st, a, head, __builtin_amdgcn_readfirstlane(list[0]), tid);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and the first tile are in registers on every path
 
   // Only the last kept tile can be partial (lists are increasing): full tiles
   // run the loop without key masking, a partial one runs after it.
-  const bool tail = n_tiles > 0 && list[n_tiles - 1] >= last_full;
+  const bool tail = n_tiles > 0 && __builtin_amdgcn_readfirstlane(list[n_tiles - 1]) >= last_full;
   const int n_main = n_tiles - (tail ? 1 : 0);
+  // Iteration i fetches tile i+1 (past the end: tile i again, never staged).
+  // kvi8r modes read that index one iteration earlier, so the read has long
+  // completed when it is used (its wait falls where the previous tile's data
+  // is needed anyway).  The exact mode reads it in place: its staging
+  // registers leave no room to carry the index across the iteration.
+  int nxt_idx = MODE != 0 && n_tiles > 0 ? list[n_tiles > 1 ? 1 : 0] : 0;
   for (int i = 0; i < n_main; ++i) {
     store_tile<MODE, NT>(st, lds_k, lds_v, lds_c, sl2, tid);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    const int nxt = list[i + 1 < n_tiles ? i + 1 : i];  // past the end: reload this tile, never staged
+    int nxt;
+    if constexpr (MODE == 0) {
+      nxt = list[i + 1 < n_tiles ? i + 1 : i];
+    } else {
+      nxt = __builtin_amdgcn_readfirstlane(nxt_idx);
+      nxt_idx = list[i + 2 < n_tiles ? i + 2 : n_tiles - 1];
+    }
     load_tile_v<MODE, NT>(st, a, head, nxt, tid);
     __builtin_amdgcn_sched_barrier(0);
     qk_block<MODE>(rb, lk);
@@ -639,7 +653,7 @@ __device__ __forceinline__ void attn_fwd_sparse_body(const AttnChunk& a, int32_t
   if (tail) {
     store_tile<MODE, NT>(st, lds_k, lds_v, lds_c, sl2, tid);
     __syncthreads();
-    const int n_valid = (int)(a.s_kv - (int64_t)list[n_main] * kTile);
+    const int n_valid = (int)(a.s_kv - (int64_t)__builtin_amdgcn_readfirstlane(list[n_main]) * kTile);
     qk_block<MODE>(rb, lk);
     softmax_block<MODE, true>(rb, lds_c, sl2, n_valid, g);
     pv_block<MODE>(rb, lv);
