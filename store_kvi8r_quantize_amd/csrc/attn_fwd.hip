@@ -884,47 +884,65 @@ __global__ __launch_bounds__(256) void route_build_kernel(const uint8_t* __restr
   if (tid == 255) counts[head * n_qt + qt] = part[255];
 }
 
-// Tile means for the Sol residual: one workgroup per (KV tile, head); threads
-// 0-127 average the tile's keys and 128-255 its values, dimension by
-// dimension, in fp32 over the dequantised store (a kvi8r code times its fp16
-// scale is exact in fp32).  The mean value is rounded to the matrix-core type.
-// The mean key is first divided by a power of two 2^e chosen so that its
-// largest magnitude lies in [64, 128) -- an exact step -- then rounded, which
-// keeps fp16 from overflowing on large keys; 2^e goes to kmscale.
+// Tile means for the Sol residual: one workgroup per (KV tile, head).  Threads
+// 0-127 sum the tile's keys and 128-255 its values, in fp32 over the
+// dequantised store (a kvi8r code times its fp16 scale is exact in fp32): each
+// thread takes 4 consecutive dimensions of every 4th row (4 row groups), and
+// the 4 partial sums of a dimension are added in a fixed order through LDS.
+// The mean value is rounded to the matrix-core type.  The mean key is first
+// divided by a power of two 2^e chosen so that its largest magnitude lies in
+// [64, 128) -- an exact step -- then rounded, which keeps fp16 from
+// overflowing on large keys; 2^e goes to kmscale.
 template <int MODE>
 __global__ __launch_bounds__(256) void tile_means_kernel(const void* __restrict__ k, const void* __restrict__ v,
                                                          const uint16_t* __restrict__ k_scale,
                                                          const uint16_t* __restrict__ v_scale, int64_t s_kv,
                                                          int32_t n_heads, uint16_t* __restrict__ kmean,
                                                          uint16_t* __restrict__ vmean, float* __restrict__ kmscale) {
+  __shared__ float part[2][4][kHeadDim];  // [K|V][row group][dim]
   __shared__ float wmax[2];
   const int t = blockIdx.x, head = blockIdx.y, tid = threadIdx.x;
   const int n_kt = (int)gridDim.x;
-  const int d = tid & (kHeadDim - 1);
-  const bool is_v = tid >= kHeadDim;
+  const int side = tid >> 7;              // 0 = K, 1 = V
+  const int rg = (tid >> 5) & 3, d4 = 4 * (tid & 31);
   const int64_t r0 = (int64_t)t * kTile;
   const int n = (int)(s_kv - r0 < kTile ? s_kv - r0 : kTile);  // >= 1
-  float sum = 0.0f;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if constexpr (MODE == 0) {
-    const uint16_t* src = static_cast<const uint16_t*>(is_v ? v : k) + (r0 * n_heads + head) * kHeadDim + d;
-    for (int r = 0; r < n; ++r) sum += bf16lo_to_f32(src[(int64_t)r * n_heads * kHeadDim]);
+    const uint16_t* src = static_cast<const uint16_t*>(side ? v : k) + (r0 * n_heads + head) * kHeadDim + d4;
+    for (int r = rg; r < n; r += 4) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(src + (int64_t)r * n_heads * kHeadDim);
+      acc[0] += bf16lo_to_f32(w[0]);
+      acc[1] += bf16hi_to_f32(w[0]);
+      acc[2] += bf16lo_to_f32(w[1]);
+      acc[3] += bf16hi_to_f32(w[1]);
+    }
   } else {
-    constexpr int G = MODE == 2 ? 4 : 1;  // scales per row; dimension d uses scale d / 32 of kvi8r32
+    constexpr int G = MODE == 2 ? 4 : 1;  // scales per row; dims d4..d4+3 lie in group d4 / 32 of kvi8r32
     const int64_t hr = (int64_t)head * s_kv + r0;
-    const int8_t* src = static_cast<const int8_t*>(is_v ? v : k) + hr * kHeadDim + d;
-    const uint16_t* sc = (is_v ? v_scale : k_scale) + hr * G + (G == 4 ? d >> 5 : 0);
-    for (int r = 0; r < n; ++r)
-      sum += (float)src[(int64_t)r * kHeadDim] * (float)__builtin_bit_cast(_Float16, sc[r * G]);
+    const int8_t* src = static_cast<const int8_t*>(side ? v : k) + hr * kHeadDim + d4;
+    const uint16_t* sc = (side ? v_scale : k_scale) + hr * G + (G == 4 ? d4 >> 5 : 0);
+    for (int r = rg; r < n; r += 4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(src + (int64_t)r * kHeadDim);
+      const float f = (float)__builtin_bit_cast(_Float16, sc[r * G]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += (float)(int8_t)(w >> (8 * e)) * f;
+    }
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) part[side][rg][d4 + e] = acc[e];
+  __syncthreads();
+  const int d = tid & (kHeadDim - 1);
+  const float sum = (part[side][0][d] + part[side][1][d]) + (part[side][2][d] + part[side][3][d]);
   const float mean = sum / (float)n;
   const int64_t o = ((int64_t)head * n_kt + t) * kHeadDim + d;
-  if (is_v) vmean[o] = (uint16_t)(Operand<MODE>::pack(mean, 0.0f) & 0xFFFFu);
+  if (side) vmean[o] = (uint16_t)(Operand<MODE>::pack(mean, 0.0f) & 0xFFFFu);
   float amax = fabsf(mean);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  if (!is_v && (tid & 63) == 0) wmax[tid >> 6] = amax;
+  if (!side && (tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
-  if (!is_v) {
+  if (!side) {
     const float mx = fmaxf(wmax[0], wmax[1]);
     int e = 0;
     if (mx > 0.0f) (void)frexpf(mx, &e);  // mx = f * 2^e, f in [0.5, 1)
