@@ -76,29 +76,40 @@ KERNEL_SOURCES = ("store_kvi8r_quantize_amd/csrc/attn_fwd.hip", "store_kvi8r_qua
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_long217k_hbm_traffic.txt")
 
 
+def kernel_source_digest() -> str:
+    """sha256 of the attention kernel sources with comments and blank space removed, so that an edit of
+    comments alone keeps the digest (and the counters taken on the code) while any code change alters it."""
+    import hashlib
+    import re
+
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)       # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                    # line comments (no // inside strings here)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(mode: str):
     """HBM bytes per launch of the attention kernel from the committed FETCH_SIZE / WRITE_SIZE summary.
 
-    The summary records the sha256 of the kernel sources it was taken on; if the
-    sources have changed since, the figure no longer describes this kernel and
-    None is returned.
+    The summary records the digest of the kernel sources it was taken on
+    (kernel_source_digest); if the code has changed since, the figure no longer
+    describes this kernel and None is returned.
     """
-    import hashlib
-
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+    digest = kernel_source_digest()
     vals = {}
     for line in text.splitlines():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.split()[0] if v.split() else ""
-    if vals.get("source_sha256") != h.hexdigest():
+    if vals.get("source_digest") != digest:
         return None
     v = vals.get(f"traffic_bytes_per_launch {mode}")
     return float(v) if v else None

@@ -7,7 +7,12 @@
 // store options": a K/V block dequant is one int8 -> fp16 cast times the row
 // scale, attention in fp16 with an online-softmax combine), optionally
 // restricted to the kept 64Q x 64KV tiles of a mask ("H3-Optimizations" page,
-// Nodes: routed 64Q x 64KV geometry, hard arm drops rejected tiles).
+// Nodes: routed 64Q x 64KV geometry, hard arm drops rejected tiles), with the
+// dropped tiles optionally entering as block-mean pseudo-keys (the Sol arm of
+// that paragraph).  Also here: the kept/dropped tile lists, the tile means of
+// the Sol arm, and a dense variant that takes the K/V store one block at a
+// time and carries the softmax state through memory between blocks (a store
+// held in host memory; node page, kv_block row).
 //
 // MI355X design
 //   * Dense: workgroup = 8 waves x 32 query rows = 256 rows of one head, two
@@ -32,8 +37,8 @@
 //     values, "Low VRAM, low RAM", "What is next") has four scales per key, so
 //     its K is dequantised to fp16 in LDS like V.
 //   * LDS: K [key][dim] and V^T [dim][key], rows padded so fragment reads are
-//     bank-conflict free; triple-buffered in the dense kernel (102 KB),
-//     double-buffered in the sparse one.
+//     bank-conflict free; triple-buffered in the dense kernel (103 KB), one
+//     buffer in the sparse one (35 KB, four workgroups per CU).
 //   * Softmax: exponents are taken against the running max already held,
 //     p = exp2(score * c - m), in one fma.  Only when a row's tile sum of p
 //     exceeds 2^8 (always on the first tile) does that row recompute its max,
