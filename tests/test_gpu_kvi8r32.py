@@ -6,8 +6,9 @@ values, finer than per row.  Quantisation: codes equal the oracle's with at most
 1e-4 off by one (rounding ties), scales within 1 fp16 ulp, closed form exact,
 chunked build bitwise.  Attention: the tolerances of kvi8r (relative L2 <= 2e-3,
 max abs <= 1e-2 against the oracle on the same store), q_chunk bitwise, all-ones
-mask == dense bitwise, the Sol arm against its oracle; and on outlier keys the
-finer store lands closer to unquantised attention than the per-row store.
+mask == dense bitwise, the Sol arm against its oracle, sampled rows of the full
+217088-token store; and on outlier keys the finer store lands closer to
+unquantised attention than the per-row store.
 """
 import numpy as np
 import pytest
@@ -180,3 +181,19 @@ def test_finer_scales_land_closer_to_unquantised_attention():
     e32, e8 = rel_l2(np.concatenate(g32), ref), rel_l2(np.concatenate(g8), ref)
     say("against unquantised attention: kvi8r32", e32, "kvi8r", e8)
     assert e32 < e8
+
+
+@pytest.mark.timeout(900)
+def test_long217k_sampled_rows():
+    # the full 217088-token store, built in kv_chunk pieces; 256 seeded rows on 4 heads against all keys
+    from gpu_common import HeadSource
+
+    w = synth.WORKLOADS["long217k"]
+    say("generating", w.name)
+    g = gpu_inputs(w)
+    store = _store32(g["k"], g["v"], kv_chunk=w.q_chunk)
+    del g["k"], g["v"]
+    out = _attend(g["q"], store, w.q_chunk)
+    src = HeadSource(w)
+    _check_rows(lambda h: src("q", h), store, out, (0, 11, 22, 31), lambda h: synth.sampled_rows(w, h, 256),
+                "long217k32")
