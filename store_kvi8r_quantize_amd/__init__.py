@@ -269,7 +269,8 @@ def h3a_attention_host_kv(q, k_host, v_host, scales_host, out, *, q_chunk: int, 
     for name, t in (("k_host", k_host), ("v_host", v_host), ("scales_host", scales_host)):
         if t is None:
             continue
-        if t.device.type != "cpu" or not t.is_pinned() or not t.is_contiguous():
+        # an empty store has no storage to pin; the library reads nothing from it
+        if t.device.type != "cpu" or not t.is_contiguous() or (t.numel() > 0 and not t.is_pinned()):
             raise ValueError(f"{name} must be a contiguous pinned CPU tensor")
     if k_host.dtype != want or v_host.dtype != want:
         raise ValueError(f"k_host / v_host must be {want} for mode {mode}")

@@ -61,6 +61,7 @@ def _staged(mode, q, store, q_chunk, kv_block):
     (257, 129, 1, 1000, 4096),    # one block holding the whole store
     (65, 1, 2, 64, 64),           # a single key
     (300, 640, 2, 128, 0),        # kv_block 0: the default 16384, one block
+    (300, 0, 2, 128, 64),         # an empty store: every row is zero, as on the device
 ])
 def test_staged_equals_device_resident_bitwise(mode, s, s_kv, heads, q_chunk, kv_block):
     w = synth.Workload("staged", max(s, s_kv), heads, 51, 256, 0)

@@ -156,3 +156,27 @@ def test_sol_sparse64k_sampled_rows(mode):
         got.append(_rows_out(out, rows, h))
         ref.append(_sol_ref(mode, src, store, h, rows, mask[h]))
     _assert_close(mode, np.concatenate(got), np.concatenate(ref), "sol-sparse64k")
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_sol_single_short_tile(mode):
+    # s_kv = 40: one KV tile of 40 keys.  q-tile 0 drops it, so its only key is the pseudo-key
+    # (softmax weight 1) and all its rows give the same output, the tile's mean value; q-tile 1
+    # keeps it.  Every row against the oracle.
+    w = synth.Workload("sol-short", 100, 2, 17, 64, 0)
+    bits = synth.qkv_bf16(w)
+    bits["k"], bits["v"] = bits["k"][:40], bits["v"][:40]
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    mask = np.ones((2, 2, 1), dtype=np.uint8)
+    mask[:, 0, 0] = 0
+    store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, 64, torch.from_numpy(mask).cuda())
+    rows = np.arange(100)
+    got, ref = [], []
+    for h in range(2):
+        got.append(_rows_out(out, rows, h))
+        ref.append(_sol_ref(mode, lambda t, hh: bits[t][:, hh], store, h, rows, mask[h]))
+    _assert_close(mode, np.concatenate(got), np.concatenate(ref), "sol-short")
+    for h in range(2):
+        first = got[h][:64]
+        assert np.array_equal(first, np.broadcast_to(first[0], first.shape))
