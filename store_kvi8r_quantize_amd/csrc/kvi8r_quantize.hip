@@ -11,11 +11,14 @@
 // rotated values gets its own fp16 scale and its codes are taken against it;
 // scales are stored [n_heads, s_total, 4].
 //
-// Layout on MI355X: one workgroup = 4 waves = 64 tokens of one head; a row is
-// handled by 4 lanes holding 32 values each, so 5 of the 7 butterfly stages
-// stay in registers and 2 use quad DPP moves.  Loads are 64 contiguous bytes
-// per lane group; codes of the 64 tokens form one contiguous 8 KB run of the
-// head-major store.  The kernel is HBM-bound: 256 B read + 130 B written per row.
+// Layout on MI355X: one workgroup = 4 waves = 64 rows = 8 tokens x 8 heads; a
+// row is handled by 4 lanes holding 32 values each, so 5 of the 7 butterfly
+// stages stay in registers and 2 use quad DPP moves.  The 8 heads of a token
+// are adjacent in the input, so a workgroup reads 8 runs of 2 KB, and writes
+// per head a run of 8 x 128 B codes in the head-major store.  Consecutive
+// workgroups take consecutive head blocks of the same tokens, so the blocks
+// in flight read whole token rows.  The kernel is HBM-bound: 256 B read +
+// 130 B written per row.
 #include "h3a_device.h"
 #include "launch.h"
 
@@ -23,6 +26,8 @@ namespace h3a {
 
 namespace {
 
+constexpr int kHeadsPerBlock = 8;
+constexpr int kTokensPerBlock = 64 / kHeadsPerBlock;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds |x| < 2^22 to an integer, ties to even
 
 template <bool GROUPED>
@@ -30,17 +35,19 @@ __global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __r
                                                              int64_t x_token_stride, int64_t n_tokens,
                                                              int64_t token_offset, int64_t s_total,
                                                              int8_t* __restrict__ codes,
-                                                             uint16_t* __restrict__ scales) {
+                                                             uint16_t* __restrict__ scales, int32_t n_heads,
+                                                             uint32_t n_head_blocks) {
   const int lane = threadIdx.x & 63;
   const int sub = lane & 3;
   const int row_in_block = (threadIdx.x >> 6) * 16 + (lane >> 2);
-  const int head = blockIdx.y;
-  const int64_t t = (int64_t)blockIdx.x * 64 + row_in_block;
-  const bool valid = t < n_tokens;
+  const uint32_t hb = blockIdx.x % n_head_blocks, tb = blockIdx.x / n_head_blocks;
+  const int head = (int)hb * kHeadsPerBlock + row_in_block % kHeadsPerBlock;
+  const int64_t t = (int64_t)tb * kTokensPerBlock + row_in_block / kHeadsPerBlock;
+  const bool valid = t < n_tokens && head < n_heads;
 
   // Element j = 32k + 8*sub + e  <->  v[8k + e].
   float v[32];
-  const uint16_t* src = x + (valid ? t : 0) * x_token_stride + (int64_t)head * kHeadDim;
+  const uint16_t* src = x + (valid ? t : 0) * x_token_stride + (int64_t)(valid ? head : 0) * kHeadDim;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     u32x4 w = {0u, 0u, 0u, 0u};
@@ -119,13 +126,17 @@ hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int6
                                  int32_t n_heads, int64_t token_offset, int64_t s_total, int8_t* codes,
                                  uint16_t* scales, bool grouped, hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
-  dim3 grid((unsigned)((n_tokens + 63) / 64), (unsigned)n_heads);
+  // head blocks fastest: workgroup b covers head block b % n_head_blocks of token block b / n_head_blocks
+  const uint32_t n_head_blocks = (uint32_t)((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
+  const int64_t n_wg = (n_tokens + kTokensPerBlock - 1) / kTokensPerBlock * n_head_blocks;
+  if (n_wg > 0xFFFFFFFFll) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_wg);
   if (grouped)
     hipLaunchKernelGGL(kvi8r_quantize_kernel<true>, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
-                       token_offset, s_total, codes, scales);
+                       token_offset, s_total, codes, scales, n_heads, n_head_blocks);
   else
     hipLaunchKernelGGL(kvi8r_quantize_kernel<false>, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
-                       token_offset, s_total, codes, scales);
+                       token_offset, s_total, codes, scales, n_heads, n_head_blocks);
   return hipGetLastError();
 }
 
