@@ -12,7 +12,7 @@ import torch
 import oracle
 import store_kvi8r_quantize_amd as h3a
 import synth
-from gpu_common import assert_quantize_ok, gpu_inputs, gpu_u16, host_u16, quantize_report, say
+from gpu_common import CODE_MISMATCH, assert_quantize_ok, gpu_inputs, gpu_u16, host_u16, quantize_report, say
 
 pytestmark = pytest.mark.gpu
 
@@ -141,3 +141,32 @@ def test_long217k_full_store_sampled_heads():
         rep = quantize_report(synth.head_bf16(w, "k", h), codes[h].cpu().numpy(), host_u16(scales[h]))
         say("long217k", h, rep)
         assert_quantize_ok(rep)
+
+
+@pytest.mark.parametrize("grouped", [False, True])
+@pytest.mark.parametrize("n_heads", [3, 5, 12, 20])
+def test_head_counts_off_the_block_size(n_heads, grouped):
+    # Workgroups cover 8 tokens x 8 heads; head counts that leave a partial head block, written at a token
+    # offset into a larger store filled with a sentinel: every row against the oracle, nothing else touched.
+    n, off, total = 333, 17, 400
+    w = synth.Workload("heads", n, n_heads, 60 + n_heads, 256, 0)
+    x = synth.qkv_bf16(w, ("k",))["k"]
+    g = 4 if grouped else 1
+    codes = torch.full((n_heads, total, 128), 99, dtype=torch.int8, device="cuda")
+    scales = torch.full((n_heads, total, g) if grouped else (n_heads, total), 3.0, dtype=torch.float16, device="cuda")
+    h3a.h3a_kv_quantize(gpu_u16(x), codes, scales, token_offset=off)
+    torch.cuda.synchronize()
+    cg, sg = codes.cpu().numpy(), host_u16(scales)
+    outside = np.r_[0:off, off + n:total]
+    assert np.all(cg[:, outside] == 99) and np.all(sg[:, outside] == 0x4200)  # fp16 3.0
+    for h in range(n_heads):
+        if grouped:
+            c_o, s_o, y = oracle.quantize_rows_grouped(oracle.bf16_to_f64(x[:, h]))
+            s_h = sg[h, off:off + n].reshape(n, 4)
+            assert np.abs(s_h.astype(np.int64) - s_o.astype(np.int64)).max() <= 1
+            same = oracle.codes_for_scales(y.reshape(-1, 32), s_h.reshape(-1)).reshape(n, 128)
+            got = cg[h, off:off + n].astype(np.int64)
+            assert np.abs(got - same).max() <= 1 and np.count_nonzero(got != same) / got.size <= CODE_MISMATCH
+            assert np.count_nonzero(got != c_o) / got.size <= CODE_MISMATCH
+        else:
+            assert_quantize_ok(quantize_report(x[:, h], cg[h, off:off + n], sg[h, off:off + n]))
