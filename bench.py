@@ -9,9 +9,10 @@ One step = one pass of the whole path over one batch of synthetic input at
   3. exact attention: h3a_attention on the bf16 store.
 Inputs are resident in HBM before timing.  After the timed steps, extra legs
 (each its own JSON object) time the per-row routed call (exact_av_rows), the
-host-staged K/V call (store in pinned host memory, PCIe-inclusive) and the
-per-32-value store (kvi8r32) at long217k, and the hard and Sol arms of the
-block-sparse path at sparse64k.
+host-staged K/V call (store in pinned host memory, PCIe-inclusive), the
+per-32-value store (kvi8r32) and one GPU's share of an 8-way head split (4 of
+the 32 heads, q_chunk 16384 and 65536) at long217k, and the hard and Sol arms
+of the block-sparse path at sparse64k.
 `value` is the algorithmic attention throughput of the step,
 2 x 4*S*S*H*128 flop over the step's wall time.
 
@@ -306,6 +307,47 @@ def host_kv_leg(h3a, w, x, store, dev_ms: dict, stream, reps: int = 1):
     return {"workload": w.name, "kv_block": w.kv_block, "q_chunk": w.q_chunk, **res}
 
 
+def shard_leg(h3a, w, x, stream, heads: int = 4, reps: int = 2):
+    """One GPU's share of the workload split by heads over 8 GPUs: the same S, heads 0..3, a store built
+    for them, attention at q_chunk 16384 and 65536 (the grid has one workgroup per 256 rows and head)."""
+    import torch
+
+    xs = {t: x[t][:, :heads].contiguous() for t in ("q", "k", "v")}
+    kc, vc, sc = h3a.new_kvi8r_store(w.seq, heads, device=xs["q"].device)
+    for t0 in range(0, w.seq, w.q_chunk):
+        h3a.h3a_kv_quantize(xs["k"][t0:t0 + w.q_chunk], kc, sc[0], token_offset=t0)
+        h3a.h3a_kv_quantize(xs["v"][t0:t0 + w.q_chunk], vc, sc[1], token_offset=t0)
+    out = torch.empty_like(xs["q"])
+    flops = 4.0 * w.seq * w.seq * heads * 128
+    res = {"workload": w.name, "seq": w.seq, "heads": heads, "share_of": f"{w.heads} heads over {w.heads // heads} GPUs"}
+    for q_chunk in (w.q_chunk, 4 * w.q_chunk):
+        ws_bytes = max(h3a.h3a_attention_workspace_bytes(w.seq, w.seq, heads, q_chunk, m, False)
+                       for m in ("kvi8r", "exact"))
+        ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=xs["q"].device)
+        calls = {
+            "kvi8r": lambda: h3a.h3a_attention(xs["q"], kc, vc, sc, out, q_chunk=q_chunk, kv_block=w.kv_block,
+                                               mode="kvi8r", workspace=ws),
+            "exact": lambda: h3a.h3a_attention(xs["q"], xs["k"], xs["v"], None, out, q_chunk=q_chunk,
+                                               kv_block=w.kv_block, mode="exact", workspace=ws),
+        }
+        entry = {"workgroups_per_launch": -(-min(q_chunk, w.seq) // 256) * heads}
+        for mode, call in calls.items():
+            call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            entry[mode] = {"ms": round(ms, 3), "tflops": round(flops / (ms / 1000) / 1e12, 2),
+                           "frac_of_peak": round(flops / (ms / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4)}
+        res[f"q_chunk_{q_chunk}"] = entry
+        del ws
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +363,8 @@ def main() -> int:
     ap.add_argument("--no-routed", action="store_true", help="skip the per-row routed (exact_av_rows) leg")
     ap.add_argument("--no-kvi8r32", action="store_true", help="skip the per-32-value store (kvi8r32) leg")
     ap.add_argument("--no-host-kv", action="store_true", help="skip the host-staged K/V leg")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the one-GPU-share leg (4 of the 32 heads, as with 8 GPUs split by heads)")
     ap.add_argument("--sparse-only", action="store_true",
                     help="run only the block-sparse legs and print their JSON (for profiling the sparse kernels)")
     args = ap.parse_args()
@@ -464,6 +508,12 @@ def main() -> int:
         del out_r
         res["long217k_kvi8r32"] = kvi8r32_leg(h3a, w, x, ws, stream)
         log(f"kvi8r32: attention {res['long217k_kvi8r32']['tflops']} TFLOP/s")
+    if not args.no_shard:
+        log("head-shard leg ...")
+        res["long217k_h4_shard"] = shard_leg(h3a, w, x, stream)
+        sh = res["long217k_h4_shard"]
+        log("head shard (4 heads): " + ", ".join(f"{k} kvi8r {v['kvi8r']['tflops']} exact {v['exact']['tflops']}"
+                                                 for k, v in sh.items() if k.startswith("q_chunk")))
     if not args.no_sparse:
         log("sparse64k leg ...")
         del x, out_e, ws
