@@ -154,8 +154,14 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
       // kvi8r32: the scale of the unit's 32-value group (dims 16*(u&7)..)
       if constexpr (MODE == 2) st.ks[j] = __builtin_amdgcn_raw_buffer_load_b16(rks, ((u >> 3) * G + ((u & 7) >> 1)) * 2, 0, 0);
     }
-    if constexpr (MODE == 1)  // one scale per key: threads 0-63 (the first wave) fetch them
-      if (tid < kTile) st.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(rks, tid * 2, 0, 0);
+    // One scale per key: the first wave (threads 0-63) fetches them.  The test
+    // is made on a wave-uniform value so the branch is a scalar one: under an
+    // exec-mask branch the compiler merges this descriptor's size with the V
+    // scales' and then moves both into vector registers, and every V-scale
+    // load becomes a readfirstlane loop.
+    if constexpr (MODE == 1)
+      if (__builtin_amdgcn_readfirstlane(tid) < kTile)
+        st.ks[0] = __builtin_amdgcn_raw_buffer_load_b16(rks, tid * 2, 0, 0);
   }
 }
 
@@ -263,8 +269,9 @@ __device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16) = c0;
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
   }
-  if constexpr (MODE == 1)
-    if (tid < kTile) lc[tid] = (float)__builtin_bit_cast(_Float16, (uint16_t)st.ks[0]) * sl2;
+  if constexpr (MODE == 1)  // the first wave, tested wave-uniformly as in load_tile_k
+    if (__builtin_amdgcn_readfirstlane(tid) < kTile)
+      lc[tid] = (float)__builtin_bit_cast(_Float16, (uint16_t)st.ks[0]) * sl2;
 }
 
 template <int MODE, int NT>
