@@ -231,13 +231,20 @@ __device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& 
 // plus compile-time offsets:
 //   K  [64 keys][128 dims], row stride 136 elements (272 B): the 16 lanes of a
 //      ds_read_b128 pass hit rows r..r+15 at banks 4r mod 64, disjoint;
-//   V^T[128 dims][64 keys], row stride 68 elements (136 B): the 32 lanes of a
-//      ds_read_b64 pass hit banks 2*(17 d mod 32), disjoint.
+//   V^T[128 rows][64 keys], row stride 68 elements (136 B): the 32 lanes of a
+//      ds_read_b64 pass hit banks 2*(17 r mod 32), disjoint.  Row r holds dim
+//      4*(r % 32) + r / 32 (vt_row below), so the staging writes of 32 lanes,
+//      which hold dims 4*dg + i for dg = 0..31, also land on rows 32*i + dg at
+//      disjoint banks; the O^T accumulator rows follow the same order, which
+//      store_rows undoes.
 //   kvi8r score factors: lc[key] = key scale * softmax_scale * log2(e).
 constexpr int kKStride = kHeadDim + 8;  // elements
 constexpr int kVStride = kTile + 4;     // elements
 constexpr int kKTileElems = kTile * kKStride;
 constexpr int kVTileElems = kHeadDim * kVStride;
+
+// V^T row of head dimension d.
+__device__ __forceinline__ constexpr int vt_row(int d) { return 32 * (d & 3) + (d >> 2); }
 
 template <int MODE, int NT>
 __device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t* lk, float* lc, float sl2, int tid) {
@@ -302,10 +309,7 @@ __device__ __forceinline__ void store_tile_v(const Stage<MODE, NT>& st, uint16_t
     t[2] = u32x2{__builtin_amdgcn_perm(p23[1], p23[0], 0x05040100u), __builtin_amdgcn_perm(p23[3], p23[2], 0x05040100u)};
     t[3] = u32x2{__builtin_amdgcn_perm(p23[1], p23[0], 0x07060302u), __builtin_amdgcn_perm(p23[3], p23[2], 0x07060302u)};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d = 4 * dg + i;
-      *reinterpret_cast<u32x2*>(lv + d * kVStride + 4 * kvg) = t[i];
-    }
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x2*>(lv + vt_row(4 * dg + i) * kVStride + 4 * kvg) = t[i];
   }
 }
 
@@ -367,7 +371,7 @@ __device__ __forceinline__ void stage_pseudo_tile(const AttnChunk& a, const SolA
     const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      lv[(8 * d8 + i) * kVStride + r] = (uint16_t)((i & 1) ? w[i >> 1] >> 16 : w[i >> 1] & 0xFFFFu);
+      lv[vt_row(8 * d8 + i) * kVStride + r] = (uint16_t)((i & 1) ? w[i >> 1] >> 16 : w[i >> 1] & 0xFFFFu);
   }
 }
 
@@ -375,7 +379,7 @@ __device__ __forceinline__ void stage_pseudo_tile(const AttnChunk& a, const SolA
 // halves g = 0, 1 of the wave hold the same query, different keys / dims).
 struct RowBlock {
   u32x4 q[8];      // B operand of S^T = K Q^T: Q[row][16t + 8g .. 16t + 8g + 7]
-  f32x16 acc[4];   // O^T accumulator: dims 32*db + 8*(j/4) + 4g + j%4, this lane's row
+  f32x16 acc[4];   // O^T accumulator: V^T rows 32*db + 8*(j/4) + 4g + j%4 (see vt_row), this lane's query
   f32x16 s[2];     // S^T of the current tile: key 32*kb + 8*(j/4) + 4g + j%4
   u32x4 pf[2][2];  // packed P of the current tile, B operand of O^T += V^T P^T
   float m, l;      // running max (log2 units) and row sum of this lane's keys
@@ -557,20 +561,19 @@ __device__ __forceinline__ void store_rows(const RowBlock& rb, const AttnChunk& 
   if (!rb.valid) return;
   const int64_t base = (rb.row * a.n_heads + head) * kHeadDim;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = 32 * db + 8 * rg + 4 * g;  // accumulator registers 4rg..4rg+3 = dims d0..d0+3
-      const float o0 = rb.acc[db][4 * rg] * inv, o1 = rb.acc[db][4 * rg + 1] * inv;
-      const float o2 = rb.acc[db][4 * rg + 2] * inv, o3 = rb.acc[db][4 * rg + 3] * inv;
-      if constexpr (MODE == 0) {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + base + d0) =
-            u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-      } else {
-        *reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + base + d0) =
-            u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
-      }
+  for (int j = 0; j < 16; ++j) {
+    // register j of block db is O^T row 32*db + x, x = 8*(j/4) + 4g + j%4, which holds dim 4x + db
+    const int d0 = 4 * (8 * (j >> 2) + 4 * g + (j & 3));
+    const float o0 = rb.acc[0][j] * inv, o1 = rb.acc[1][j] * inv;
+    const float o2 = rb.acc[2][j] * inv, o3 = rb.acc[3][j] * inv;
+    if constexpr (MODE == 0) {
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + base + d0) =
+          u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+    } else {
+      *reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + base + d0) =
+          u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
     }
+  }
 }
 
 // Block-sparse kernel: one workgroup = 2 waves x 32 rows = one 64-row routing
