@@ -124,3 +124,21 @@ def test_staged_long217k_kvi8r_bitwise():
     dev = _device("kvi8r", g["q"], store, w.q_chunk)
     got = _staged("kvi8r", g["q"], store, w.q_chunk, w.kv_block)
     assert torch.equal(got.view(torch.int16), dev.view(torch.int16))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_staged_long217k_wide_q_chunk_bitwise(mode):
+    """The bench's wider host-staged setting: q_chunk 65536 (four query chunks, so four passes of the store
+    over PCIe) gives the bits of the resident call at q_chunk 16384."""
+    w = synth.WORKLOADS["long217k"]
+    say("generating", w.name, "mode", mode)
+    g = gpu_inputs(w)
+    if mode == "kvi8r":
+        store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk)
+        del g["k"], g["v"]
+    else:
+        store = (g.pop("k"), g.pop("v"), None)
+    dev = _device(mode, g["q"], store, w.q_chunk)
+    got = _staged(mode, g["q"], store, 65536, w.kv_block)
+    assert torch.equal(got.view(torch.int16), dev.view(torch.int16))
