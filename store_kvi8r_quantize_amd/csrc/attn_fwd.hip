@@ -779,21 +779,23 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
   const float sl2 = a.scale_log2;
   const bool tail = n > 0 && (int64_t)n * kTile > a.s_kv;  // the last tile is partial
   const int n_valid_last = n > 0 ? (int)(a.s_kv - (int64_t)(n - 1) * kTile) : 0;
-  auto lk = [&](int t) { return lds_k[t % 3] + c * kKStride + 8 * g; };
-  auto lv = [&](int t) { return lds_v[t % 3] + c * kVStride + 4 * g; };
-  auto lc = [&](int t) -> const float* { return lds_c[t % 3]; };
-  auto sm_full = [&](int t) { softmax_block<MODE, false>(rb, lc(t), sl2, kTile, g); };
-  auto sm_last = [&](int t) {
+  // Buffer b of tile t is t % 3; callers pass b, kept in scalar registers.
+  auto lk = [&](int b) { return lds_k[b] + c * kKStride + 8 * g; };
+  auto lv = [&](int b) { return lds_v[b] + c * kVStride + 4 * g; };
+  auto lc = [&](int b) -> const float* { return lds_c[b]; };
+  auto next3 = [](int b) { return __builtin_amdgcn_readfirstlane(b == 2 ? 0 : b + 1); };
+  auto sm_full = [&](int b) { softmax_block<MODE, false>(rb, lc(b), sl2, kTile, g); };
+  auto sm_last = [&](int b) {
     if (tail)
-      softmax_block<MODE, true>(rb, lc(t), sl2, n_valid_last, g);
+      softmax_block<MODE, true>(rb, lc(b), sl2, n_valid_last, g);
     else
-      softmax_block<MODE, false>(rb, lc(t), sl2, kTile, g);
+      softmax_block<MODE, false>(rb, lc(b), sl2, kTile, g);
   };
 
   if (!late) {
     Stage<MODE, NS> st;
-    auto stage = [&](int t) {  // write tile t (held in registers) to LDS
-      store_tile<MODE, NS>(st, lds_k[t % 3], lds_v[t % 3], lds_c[t % 3], sl2, tid);
+    auto stage = [&](int b) {  // write the tile held in registers to buffer b
+      store_tile<MODE, NS>(st, lds_k[b], lds_v[b], lds_c[b], sl2, tid);
     };
     if (n > 0) {
       load_tile<MODE, NS>(st, a, head, 0, tid);
@@ -802,26 +804,29 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q and tile 0 are in registers on every path
     if (n > 1) load_tile<MODE, NS>(st, a, head, 1, tid);
     __syncthreads();
+    int bi = 0;  // buffer of tile i
     for (int i = 0; i + 1 < n; ++i) {  // periods 0 .. n-2
-      qk_block<MODE>(rb, lk(i));
+      const int bn = next3(bi);
+      qk_block<MODE>(rb, lk(bi));
       __builtin_amdgcn_sched_barrier(0);
-      sm_full(i);
+      sm_full(bi);
       __builtin_amdgcn_sched_barrier(0);
-      pv_block<MODE>(rb, lv(i));
+      pv_block<MODE>(rb, lv(bi));
       __builtin_amdgcn_sched_barrier(0);
-      stage(i + 1);
+      stage(bn);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       // tile i+2; past the end, reload the last tile (never staged)
       load_tile<MODE, NS>(st, a, head, i + 2 < n ? i + 2 : n - 1, tid);
       __builtin_amdgcn_sched_barrier(0);
+      bi = bn;
     }
     if (n > 0) {  // period n-1
-      qk_block<MODE>(rb, lk(n - 1));
+      qk_block<MODE>(rb, lk(bi));
       __builtin_amdgcn_sched_barrier(0);
-      sm_last(n - 1);
+      sm_last(bi);
       __builtin_amdgcn_sched_barrier(0);
-      pv_block<MODE>(rb, lv(n - 1));
+      pv_block<MODE>(rb, lv(bi));
       __syncthreads();
     }
     __syncthreads();  // period n: group 1 finishes tile n-1
@@ -833,19 +838,22 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     }
+    int bp = 0;  // buffer of tile i-1
     for (int i = 1; i < n; ++i) {  // periods 1 .. n-1
-      sm_full(i - 1);
+      const int bi = next3(bp);
+      sm_full(bp);
       __builtin_amdgcn_sched_barrier(0);
-      pv_block<MODE>(rb, lv(i - 1));
+      pv_block<MODE>(rb, lv(bp));
       __builtin_amdgcn_sched_barrier(0);
-      qk_block<MODE>(rb, lk(i));
+      qk_block<MODE>(rb, lk(bi));
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
+      bp = bi;
     }
     if (n > 0) {  // period n
-      sm_last(n - 1);
+      sm_last(bp);
       __builtin_amdgcn_sched_barrier(0);
-      pv_block<MODE>(rb, lv(n - 1));
+      pv_block<MODE>(rb, lv(bp));
     }
     __syncthreads();
   }
