@@ -23,9 +23,10 @@
 //     so the softmax row sums are in-lane (plus one exchange between lanes l
 //     and l^32).  P^T then feeds O^T += V^T P^T directly from registers as the
 //     B operand; the key order inside each 16-key step is chosen to match the
-//     accumulator layout, and V^T is read from LDS in that same order.  K and
-//     V^T fragments are read from LDS four MFMAs ahead of their use, with the
-//     independent accumulator chains interleaved.
+//     accumulator layout.  V stays key-major in LDS and its V^T fragments are
+//     gathered in that same key order by transposing LDS reads
+//     (ds_read_b64_tr_b16).  K and V fragments are read from LDS four MFMAs
+//     ahead of their use, with the independent accumulator chains interleaved.
 //   * K/V tiles are fetched with buffer loads whose range check zero-fills rows
 //     past the end of the store (no per-row compares), held in registers one
 //     tile ahead, and written to LDS once per workgroup: kvi8r codes become
@@ -36,9 +37,9 @@
 //     code * scale out of the scores.  The kvi8r32 store (one scale per 32
 //     values, "Low VRAM, low RAM", "What is next") has four scales per key, so
 //     its K is dequantised to fp16 in LDS like V.
-//   * LDS: K [key][dim] and V^T [dim][key], rows padded so fragment reads are
-//     bank-conflict free; triple-buffered in the dense kernel (103 KB), one
-//     buffer in the sparse one (35 KB, four workgroups per CU).
+//   * LDS: K and V both [key][dim], rows padded so fragment reads and staging
+//     writes are bank-conflict free; triple-buffered in the dense kernel
+//     (112 KB), one buffer in the sparse one (38 KB, four workgroups per CU).
 //   * Softmax: exponents are taken against the running max already held,
 //     p = exp2(score * c - m), in one fma.  Only when a row's tile sum of p
 //     exceeds 2^8 (always on the first tile) does that row recompute its max,
@@ -113,15 +114,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 }
 
 // Per-thread staging registers for one K/V tile.  K unit = one key row x 16
-// dims; V unit = 4 keys x 4 dims.
+// dims; V unit = one key row x 8 dims.
 template <int MODE, int NT>
 struct Stage {
   static constexpr int KU = 512 / NT;
-  static constexpr int VU = 512 / NT;
+  static constexpr int VU = 1024 / NT;
   u32x4 k[KU][MODE == 0 ? 2 : 1];
   uint32_t ks[MODE == 2 ? KU : 1];  // kvi8r32: each unit's group scale; kvi8r: key tid's scale (threads 0-63)
-  uint32_t v[VU][4][MODE == 0 ? 2 : 1];
-  uint32_t vs[VU][2];  // kvi8r: fp16 scales of the unit's 4 keys, packed in pairs
+  std::conditional_t<MODE == 0, u32x4, u32x2> v[VU];  // 8 bf16 values, or 8 int8 codes
+  uint32_t vs[MODE == 0 ? 1 : VU];  // kvi8r: the unit's key scale; kvi8r32: the scale of its 32-value group
 };
 
 // Tile kt of one head: rows kt*64 .. kt*64+63 of the store; rows past s_kv read
@@ -176,13 +177,7 @@ __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
-      const int o = (4 * (u >> 5)) * rstride + 8 * (u & 31);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, o + r * rstride, 0, 0));
-        st.v[j][r][0] = w[0];
-        st.v[j][r][1] = w[1];
-      }
+      st.v[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (u >> 4) * rstride + 16 * (u & 15), 0, 0));
     }
   } else {
     constexpr int G = MODE == 2 ? 4 : 1;  // scales per row
@@ -192,30 +187,10 @@ __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
-      const int r0 = 4 * (u >> 5);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        st.v[j][r][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, (r0 + r) * kHeadDim + 4 * (u & 31), 0, 0);
-      if constexpr (MODE == 2) {  // the 4 keys' scales of this unit's 32-value group, one load each
-        const int grp = (u & 31) >> 3;
-        const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 0) * 4 + grp) * 2, 0, 0);
-        const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 1) * 4 + grp) * 2, 0, 0);
-        const uint32_t s2 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 2) * 4 + grp) * 2, 0, 0);
-        const uint32_t s3 = __builtin_amdgcn_raw_buffer_load_b16(rvs, ((r0 + 3) * 4 + grp) * 2, 0, 0);
-        st.vs[j][0] = (s0 & 0xFFFFu) | (s1 << 16);
-        st.vs[j][1] = (s2 & 0xFFFFu) | (s3 << 16);
-      } else if (left >= kTile && (hrow & 3) == 0) {  // whole tile in range, 8-byte aligned: the 4 scales in one load
-        const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, r0 * 2, 0, 0));
-        st.vs[j][0] = w[0];
-        st.vs[j][1] = w[1];
-      } else {  // partial tile or unaligned: each scale on its own, rows past the end read as 0
-        const uint32_t s0 = __builtin_amdgcn_raw_buffer_load_b16(rvs, r0 * 2, 0, 0);
-        const uint32_t s1 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + 1) * 2, 0, 0);
-        const uint32_t s2 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + 2) * 2, 0, 0);
-        const uint32_t s3 = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + 3) * 2, 0, 0);
-        st.vs[j][0] = (s0 & 0xFFFFu) | (s1 << 16);
-        st.vs[j][1] = (s2 & 0xFFFFu) | (s3 << 16);
-      }
+      const int r = u >> 4, d8 = u & 15;
+      st.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, r * kHeadDim + 8 * d8, 0, 0));
+      // kvi8r32: dims 8*d8.. lie in 32-value group d8 / 4
+      st.vs[j] = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r * G + (MODE == 2 ? d8 >> 2 : 0)) * 2, 0, 0);
     }
   }
 }
@@ -226,25 +201,20 @@ __device__ __forceinline__ void load_tile(Stage<MODE, NT>& st, const AttnChunk& 
   load_tile_v<MODE, NT>(st, a, head, kt, tid);
 }
 
-// LDS layouts (16-bit elements), rows padded so that every fragment read of a
-// wave is bank-conflict free and every lane's addresses are one base register
-// plus compile-time offsets:
-//   K  [64 keys][128 dims], row stride 136 elements (272 B): the 16 lanes of a
-//      ds_read_b128 pass hit rows r..r+15 at banks 4r mod 64, disjoint;
-//   V^T[128 rows][64 keys], row stride 68 elements (136 B): the 32 lanes of a
-//      ds_read_b64 pass hit banks 2*(17 r mod 32), disjoint.  Row r holds dim
-//      4*(r % 32) + r / 32 (vt_row below), so the staging writes of 32 lanes,
-//      which hold dims 4*dg + i for dg = 0..31, also land on rows 32*i + dg at
-//      disjoint banks; the O^T accumulator rows follow the same order, which
-//      store_rows undoes.
+// LDS layouts (16-bit elements), rows padded so that every fragment read and
+// every staging write of a wave is bank-conflict free and every lane's
+// addresses are one base register plus compile-time offsets:
+//   K [64 keys][128 dims], row stride 136 elements (272 B): the 16 lanes of a
+//     ds_read_b128 pass hit rows r..r+15 at banks 4r mod 64, disjoint;
+//   V [64 keys][128 dims], row stride 160 elements (320 B): a staging write
+//     of 16 lanes covers one row, all 64 banks; a transposed read
+//     (ds_read_b64_tr_b16, below) of 32 lanes takes rows r..r+3 at dims
+//     d0 + 16h + 4q (h = 0, 1; q = 0..3), banks 16r + 8h + 2q mod 64, disjoint.
 //   kvi8r score factors: lc[key] = key scale * softmax_scale * log2(e).
-constexpr int kKStride = kHeadDim + 8;  // elements
-constexpr int kVStride = kTile + 4;     // elements
+constexpr int kKStride = kHeadDim + 8;   // elements
+constexpr int kVStride = kHeadDim + 32;  // elements
 constexpr int kKTileElems = kTile * kKStride;
-constexpr int kVTileElems = kHeadDim * kVStride;
-
-// V^T row of head dimension d.
-__device__ __forceinline__ constexpr int vt_row(int d) { return 32 * (d & 3) + (d >> 2); }
+constexpr int kVTileElems = kTile * kVStride;
 
 template <int MODE, int NT>
 __device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t* lk, float* lc, float sl2, int tid) {
@@ -286,30 +256,18 @@ __device__ __forceinline__ void store_tile_v(const Stage<MODE, NT>& st, uint16_t
 #pragma unroll
   for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
     const int u = tid + NT * j;
-    const int kvg = u >> 5, dg = u & 31;
-    uint32_t p01[4], p23[4];  // per key row r: packed (dim0, dim1) and (dim2, dim3)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if constexpr (MODE == 0) {
-        p01[r] = st.v[j][r][0];
-        p23[r] = st.v[j][r][1];
-      } else {
-        const uint32_t sw = st.vs[j][r >> 1];
-        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)((r & 1) ? sw >> 16 : sw & 0xFFFFu));
-        const half2v s2 = {s, s};
-        const uint32_t w = st.v[j][r][0] ^ 0x80808080u;
-        p01[r] = dequant_pair(w, kSelLo, s2);
-        p23[r] = dequant_pair(w, kSelHi, s2);
-      }
+    const int r = u >> 4, d8 = u & 15;
+    u32x4 c;
+    if constexpr (MODE == 0) {
+      c = st.v[j];
+    } else {
+      const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.vs[j]);
+      const half2v s2 = {sc, sc};
+      const uint32_t w0 = st.v[j][0] ^ 0x80808080u, w1 = st.v[j][1] ^ 0x80808080u;
+      c = u32x4{dequant_pair(w0, kSelLo, s2), dequant_pair(w0, kSelHi, s2), dequant_pair(w1, kSelLo, s2),
+                dequant_pair(w1, kSelHi, s2)};
     }
-    // transpose 4 keys x 4 dims: dim i gets (key0, key1 | key2, key3)
-    u32x2 t[4];
-    t[0] = u32x2{__builtin_amdgcn_perm(p01[1], p01[0], 0x05040100u), __builtin_amdgcn_perm(p01[3], p01[2], 0x05040100u)};
-    t[1] = u32x2{__builtin_amdgcn_perm(p01[1], p01[0], 0x07060302u), __builtin_amdgcn_perm(p01[3], p01[2], 0x07060302u)};
-    t[2] = u32x2{__builtin_amdgcn_perm(p23[1], p23[0], 0x05040100u), __builtin_amdgcn_perm(p23[3], p23[2], 0x05040100u)};
-    t[3] = u32x2{__builtin_amdgcn_perm(p23[1], p23[0], 0x07060302u), __builtin_amdgcn_perm(p23[3], p23[2], 0x07060302u)};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x2*>(lv + vt_row(4 * dg + i) * kVStride + 4 * kvg) = t[i];
+    *reinterpret_cast<u32x4*>(lv + r * kVStride + 8 * d8) = c;
   }
 }
 
@@ -327,7 +285,7 @@ __device__ __forceinline__ void store_tile(const Stage<MODE, NT>& st, uint16_t* 
 // zeros.  lc[s] = kmscale * softmax_scale * log2 e and lc[kTile + s] = log2 of
 // the tile's key count, so the key's weight is count * exp(scale * q . mean).
 // First the slots' tile indices go to lt (-1 = empty), then every thread
-// fetches its K and V^T pieces with buffer loads at 32-bit offsets from the
+// fetches its K and V pieces with buffer loads at 32-bit offsets from the
 // head's tables (an empty slot's offset is past the table end and reads 0).
 template <int NT>
 __device__ __forceinline__ void stage_pseudo_tile(const AttnChunk& a, const SolArgs& sa, const int32_t* dl,
@@ -363,15 +321,13 @@ __device__ __forceinline__ void stage_pseudo_tile(const AttnChunk& a, const SolA
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
   }
 #pragma unroll
-  for (int j = 0; j < 1024 / NT; ++j) {  // V^T: unit = one slot x 8 dims, written element by element
+  for (int j = 0; j < 1024 / NT; ++j) {  // V: unit = one slot x 8 dims
     const int u = tid + NT * j;
-    const int r = u & 63, d8 = u >> 6;
+    const int r = u >> 4, d8 = u & 15;
     const int t = lt[r];
     const uint32_t o = t >= 0 ? (uint32_t)t * (kHeadDim * 2) + 16 * d8 : table;
-    const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      lv[vt_row(8 * d8 + i) * kVStride + r] = (uint16_t)((i & 1) ? w[i >> 1] >> 16 : w[i >> 1] & 0xFFFFu);
+    *reinterpret_cast<u32x4*>(lv + r * kVStride + 8 * d8) =
+        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
   }
 }
 
@@ -379,7 +335,7 @@ __device__ __forceinline__ void stage_pseudo_tile(const AttnChunk& a, const SolA
 // halves g = 0, 1 of the wave hold the same query, different keys / dims).
 struct RowBlock {
   u32x4 q[8];      // B operand of S^T = K Q^T: Q[row][16t + 8g .. 16t + 8g + 7]
-  f32x16 acc[4];   // O^T accumulator: V^T rows 32*db + 8*(j/4) + 4g + j%4 (see vt_row), this lane's query
+  f32x16 acc[4];   // O^T accumulator: dims 32*db + 8*(j/4) + 4g + j%4, this lane's row
   f32x16 s[2];     // S^T of the current tile: key 32*kb + 8*(j/4) + 4g + j%4
   u32x4 pf[2][2];  // packed P of the current tile, B operand of O^T += V^T P^T
   float m, l;      // running max (log2 units) and row sum of this lane's keys
@@ -425,9 +381,28 @@ __device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
   mfma_read_pattern<1>();
 }
 
+// Transposed LDS read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j receives element j % 4 of the 8-byte blocks addressed by lanes
+// 4k + j / 4, k = 0..3.  When lane i of the group addresses V row r0 + i / 4
+// at dims d0 + 4 (i % 4), lane j receives V[r0 + k][d0 + j], k = 0..3: four
+// keys of one dim, a column of V, as the A operand of O^T += V^T P^T needs.
+__device__ __forceinline__ u32x2 read_v_column(const uint16_t* p) {
+  typedef short short4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4v lds_short4v;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p)));
+}
+
+// This lane's address for read_v_column in a V buffer: row 4g + i / 4 and dims
+// 16h + 4 (i % 4), i = lane % 16, h = (lane / 16) % 2, so that the lane receives
+// dim 32 db + c (c = lane % 32) of keys 4g .. 4g + 3 past the row offset.
+__device__ __forceinline__ int v_lane_offset(int lane) {
+  const int i = lane & 15, h = (lane >> 4) & 1, g = lane >> 5;
+  return (4 * g + (i >> 2)) * kVStride + 16 * h + 4 * (i & 3);
+}
+
 // O^T += V^T P^T.  k-step j covers keys 32*(j/2) + 16*(j%2) + 4g + {0..3} and
 // the same + 8, matching the order of the S^T accumulator registers in pf.
-// lv points at this lane's V^T row c, keys 4g.. of the current buffer.
+// lv points at this lane's v_lane_offset in the current V buffer.
 template <int MODE>
 __device__ __forceinline__ void pv_issue(RowBlock& rb, const uint16_t* lv) {
   using Op = Operand<MODE>;
@@ -435,9 +410,9 @@ __device__ __forceinline__ void pv_issue(RowBlock& rb, const uint16_t* lv) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = i >> 2, db = i & 3;
-    const uint16_t* p = lv + 32 * db * kVStride + 32 * (j >> 1) + 16 * (j & 1);
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
+    const uint16_t* p = lv + (32 * (j >> 1) + 16 * (j & 1)) * kVStride + 32 * db;
+    const u32x2 lo = read_v_column(p);
+    const u32x2 hi = read_v_column(p + 8 * kVStride);
     va[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
 #pragma unroll
@@ -561,30 +536,31 @@ __device__ __forceinline__ void store_rows(const RowBlock& rb, const AttnChunk& 
   if (!rb.valid) return;
   const int64_t base = (rb.row * a.n_heads + head) * kHeadDim;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    // register j of block db is O^T row 32*db + x, x = 8*(j/4) + 4g + j%4, which holds dim 4x + db
-    const int d0 = 4 * (8 * (j >> 2) + 4 * g + (j & 3));
-    const float o0 = rb.acc[0][j] * inv, o1 = rb.acc[1][j] * inv;
-    const float o2 = rb.acc[2][j] * inv, o3 = rb.acc[3][j] * inv;
-    if constexpr (MODE == 0) {
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + base + d0) =
-          u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-    } else {
-      *reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + base + d0) =
-          u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * db + 8 * rg + 4 * g;  // accumulator registers 4rg..4rg+3 = dims d0..d0+3
+      const float o0 = rb.acc[db][4 * rg] * inv, o1 = rb.acc[db][4 * rg + 1] * inv;
+      const float o2 = rb.acc[db][4 * rg + 2] * inv, o3 = rb.acc[db][4 * rg + 3] * inv;
+      if constexpr (MODE == 0) {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + base + d0) =
+            u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      } else {
+        *reinterpret_cast<u32x4*>(static_cast<float*>(a.out) + base + d0) =
+            u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
+      }
     }
-  }
 }
 
 // Block-sparse kernel: one workgroup = 2 waves x 32 rows = one 64-row routing
 // q-tile of one head, iterating only the KV tiles its mask row keeps, in
-// increasing order.  A single LDS buffer (35 KB) and at most 256 registers per
+// increasing order.  A single LDS buffer (38 KB) and at most 256 registers per
 // wave let four workgroups share a CU, two waves per SIMD, so one workgroup's
 // staging and softmax run under another's matrix-core work.  Per kept tile:
 //     stage(i) [barrier] fetch(i+1), QK(i), softmax(i), PV(i) [barrier]
 // Each row's arithmetic is that of the dense kernel.  With SOL, the dropped
 // tiles then follow as pseudo-keys, 64 per pass (stage_pseudo_tile).
-// lds_k, lds_v: one K and one V^T tile; lds_c: score factors, with SOL followed
+// lds_k, lds_v: one K and one V tile; lds_c: score factors, with SOL followed
 // by the pseudo slots' biases and tile indices.
 template <int MODE, bool SOL>
 __device__ __forceinline__ void attn_fwd_sparse_body(const AttnChunk& a, int32_t n_qt, int32_t n_kt,
@@ -624,7 +600,7 @@ __device__ __forceinline__ void attn_fwd_sparse_body(const AttnChunk& a, int32_t
   const float sl2 = a.scale_log2;
   const int last_full = (int)(a.s_kv / kTile);  // tiles with index >= this one are partial
   const uint16_t* lk = lds_k + c * kKStride + 8 * g;
-  const uint16_t* lv = lds_v + c * kVStride + 4 * g;
+  const uint16_t* lv = lds_v + v_lane_offset(lane);
 
   // Kept-tile indices are the same in every lane: readfirstlane keeps the
   // buffer descriptors built from them in scalar registers.
@@ -781,7 +757,7 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
   const int n_valid_last = n > 0 ? (int)(a.s_kv - (int64_t)(n - 1) * kTile) : 0;
   // Buffer b of tile t is t % 3; callers pass b, kept in scalar registers.
   auto lk = [&](int b) { return lds_k[b] + c * kKStride + 8 * g; };
-  auto lv = [&](int b) { return lds_v[b] + c * kVStride + 4 * g; };
+  auto lv = [&](int b) { return lds_v[b] + v_lane_offset(lane); };
   auto lc = [&](int b) -> const float* { return lds_c[b]; };
   auto next3 = [](int b) { return __builtin_amdgcn_readfirstlane(b == 2 ? 0 : b + 1); };
   auto sm_full = [&](int b) { softmax_block<MODE, false>(rb, lc(b), sl2, kTile, g); };
