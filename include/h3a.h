@@ -30,6 +30,8 @@
  *   - head_dim must be 128: the width of the fixed Hadamard basis [P1 kv_store].
  *   - Token-major tensors are [tokens, n_heads, 128] with the 128 values of a
  *     (token, head) row contiguous.
+ *   - The attention calls take 1 <= n_heads <= 65536, 0 <= s_kv < 2^31 and
+ *     0 <= s_q <= 2^31; other sizes are H3A_EINVAL.
  */
 #ifndef H3A_H
 #define H3A_H

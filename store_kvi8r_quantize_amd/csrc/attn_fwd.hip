@@ -108,9 +108,23 @@ __device__ __forceinline__ uint32_t dequant_pair(uint32_t u, uint32_t sel, half2
   return __builtin_bit_cast(uint32_t, (byte_pair(u, sel) - bias) * s2);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t n = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)n, kBufWord3);
+// Buffer resource over `bytes` bytes from base; loads past them read 0.  Every
+// caller passes wave-uniform values; readfirstlane states that to the compiler,
+// which otherwise may keep the resource in vector registers and wrap each load
+// in a readfirstlane loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), kBufWord3);
+}
+
+// Rows of KV tile kt inside the store, in [0, 64].  A tile's loads span only
+// its own 64 rows, so their range check needs no more than this count, and it
+// stays in 32 bits (s_kv < 2^31, checked on the host): scalar instructions,
+// where 64-bit bounds would take vector compares on every tile.  A negative
+// kt is read as tile 0, so no buffer base can precede the store.
+__device__ __forceinline__ int32_t tile_rows(const AttnChunk& a, int kt) {
+  const int32_t left = (int32_t)a.s_kv - (kt > 0 ? kt : 0) * kTile;
+  return left < 0 ? 0 : (left > kTile ? kTile : left);
 }
 
 // Per-thread staging registers for one K/V tile.  K unit = one key row x 16
@@ -130,11 +144,11 @@ struct Stage {
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
   const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
-  const int64_t left = a.s_kv - row0;  // >= 1, or 0 for an empty store (every load then reads 0)
+  const uint32_t rows = (uint32_t)tile_rows(a, kt);  // 0 for an empty store: every load then reads 0
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;  // bytes between tokens
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
-    const auto rk = make_rsrc(static_cast<const char*>(a.k) + off0, (left - 1) * rstride + kHeadDim * 2);
+    const auto rk = make_rsrc(static_cast<const char*>(a.k) + off0, rows ? (rows - 1) * rstride + kHeadDim * 2 : 0u);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
       const int u = tid + NT * j;
@@ -145,8 +159,8 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
   } else {
     constexpr int G = MODE == 2 ? 4 : 1;  // scales per row
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
-    const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, left * kHeadDim);
-    const auto rks = make_rsrc(a.k_scale + hrow * G, left * 2 * G);
+    const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, rows * kHeadDim);
+    const auto rks = make_rsrc(a.k_scale + hrow * G, rows * 2 * G);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
       const int u = tid + NT * j;
@@ -169,11 +183,11 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
   const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
-  const int64_t left = a.s_kv - row0;  // >= 1, or 0 for an empty store (every load then reads 0)
+  const uint32_t rows = (uint32_t)tile_rows(a, kt);  // 0 for an empty store: every load then reads 0
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
-    const auto rv = make_rsrc(static_cast<const char*>(a.v) + off0, (left - 1) * rstride + kHeadDim * 2);
+    const auto rv = make_rsrc(static_cast<const char*>(a.v) + off0, rows ? (rows - 1) * rstride + kHeadDim * 2 : 0u);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
@@ -182,8 +196,8 @@ __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk
   } else {
     constexpr int G = MODE == 2 ? 4 : 1;  // scales per row
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
-    const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, left * kHeadDim);
-    const auto rvs = make_rsrc(a.v_scale + hrow * G, left * 2 * G);
+    const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, rows * kHeadDim);
+    const auto rvs = make_rsrc(a.v_scale + hrow * G, rows * 2 * G);
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;

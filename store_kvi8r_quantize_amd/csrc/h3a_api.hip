@@ -153,9 +153,11 @@ struct LaunchTimer {
 // ---- argument checks shared by the attention entry points ----------------------
 int check_shapes(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chunk, int64_t kv_block,
                  float softmax_scale) {
-  if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
+  // The kernels count a tile's rows in 32 bits and address 64 token rows of the
+  // exact store ([s_kv, n_heads, 128] bf16) with 32-bit offsets.
+  if (n_heads < 1 || n_heads > 65536) return fail(H3A_EINVAL, "n_heads must be in [1, 65536] (got %d)", n_heads);
   if (s_q < 0 || s_kv < 0) return fail(H3A_EINVAL, "s_q and s_kv must be >= 0");
-  if (s_q > ((int64_t)1 << 31) || s_kv > ((int64_t)1 << 31)) return fail(H3A_EINVAL, "sequence too long");
+  if (s_q > ((int64_t)1 << 31) || s_kv >= ((int64_t)1 << 31)) return fail(H3A_EINVAL, "sequence too long");
   if (q_chunk < 1) return fail(H3A_EINVAL, "q_chunk must be >= 1 (got %lld)", (long long)q_chunk);
   if (kv_block < 0 || kv_block % H3A_TILE != 0)
     return fail(H3A_EINVAL, "kv_block must be 0 or a positive multiple of 64 (got %lld)", (long long)kv_block);

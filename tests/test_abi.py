@@ -57,6 +57,9 @@ def _attn(lib, **kw):
     (dict(mode=3), -1, "mode"),
     (dict(mode=2, scales=None), -1, "scales"),
     (dict(n_heads=0), -1, "n_heads"),
+    (dict(n_heads=65537), -1, "n_heads"),
+    (dict(s_kv=1 << 31), -1, "sequence too long"),
+    (dict(s_q=(1 << 31) + 1), -1, "sequence too long"),
     (dict(s_q=-1), -1, "s_q"),
     (dict(q_chunk=0), -1, "q_chunk"),
     (dict(kv_block=100), -1, "kv_block"),
