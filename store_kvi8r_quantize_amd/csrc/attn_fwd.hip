@@ -117,14 +117,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            __builtin_amdgcn_readfirstlane((int)bytes), kBufWord3);
 }
 
-// Rows of KV tile kt inside the store, in [0, 64].  A tile's loads span only
-// its own 64 rows, so their range check needs no more than this count, and it
-// stays in 32 bits (s_kv < 2^31, checked on the host): scalar instructions,
-// where 64-bit bounds would take vector compares on every tile.  A negative
-// kt is read as tile 0, so no buffer base can precede the store.
-__device__ __forceinline__ int32_t tile_rows(const AttnChunk& a, int kt) {
-  const int32_t left = (int32_t)a.s_kv - (kt > 0 ? kt : 0) * kTile;
-  return left < 0 ? 0 : (left > kTile ? kTile : left);
+// Size of the buffer resource of KV tile kt: from the tile's first row to the
+// end of the store, `rows` rows of row_bytes whose last one ends after
+// last_bytes, saturated at 2^32 - 1.  The row count stays in 32 bits (s_kv <
+// 2^31, checked on the host) and the saturation tests the high word, held
+// opaque to the optimizer (an empty asm on a scalar register) so that it stays
+// a 32-bit scalar compare: folded back into a 64-bit bound, the test would take
+// vector compares on every tile.  (A resource of just
+// the tile's 64 rows also bounds every access, but with it the exact store's
+// tiles, 64 rows spread over n_heads * 256-byte token strides, fetch about 4x
+// the bytes from memory at 217088 tokens, by the FETCH_SIZE counter.)  A
+// negative kt is read as tile 0, so no buffer base can precede the store.
+__device__ __forceinline__ uint32_t store_span(const AttnChunk& a, int kt, uint32_t row_bytes, uint32_t last_bytes) {
+  const int32_t rows = (int32_t)a.s_kv - (kt > 0 ? kt : 0) * kTile;
+  if (rows <= 0) return 0u;  // an empty store: every load reads 0
+  const uint64_t b = (uint64_t)(uint32_t)(rows - 1) * row_bytes + last_bytes;
+  uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  asm("" : "+s"(hi));
+  return hi ? 0xFFFFFFFFu : (uint32_t)b;
 }
 
 // Per-thread staging registers for one K/V tile.  K unit = one key row x 16
@@ -144,11 +154,10 @@ struct Stage {
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
   const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
-  const uint32_t rows = (uint32_t)tile_rows(a, kt);  // 0 for an empty store: every load then reads 0
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;  // bytes between tokens
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
-    const auto rk = make_rsrc(static_cast<const char*>(a.k) + off0, rows ? (rows - 1) * rstride + kHeadDim * 2 : 0u);
+    const auto rk = make_rsrc(static_cast<const char*>(a.k) + off0, store_span(a, kt, rstride, kHeadDim * 2));
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
       const int u = tid + NT * j;
@@ -159,8 +168,8 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
   } else {
     constexpr int G = MODE == 2 ? 4 : 1;  // scales per row
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
-    const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, rows * kHeadDim);
-    const auto rks = make_rsrc(a.k_scale + hrow * G, rows * 2 * G);
+    const auto rk = make_rsrc(static_cast<const int8_t*>(a.k) + hrow * kHeadDim, store_span(a, kt, kHeadDim, kHeadDim));
+    const auto rks = make_rsrc(a.k_scale + hrow * G, store_span(a, kt, 2 * G, 2 * G));
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::KU; ++j) {
       const int u = tid + NT * j;
@@ -183,11 +192,10 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
   const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
-  const uint32_t rows = (uint32_t)tile_rows(a, kt);  // 0 for an empty store: every load then reads 0
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
-    const auto rv = make_rsrc(static_cast<const char*>(a.v) + off0, rows ? (rows - 1) * rstride + kHeadDim * 2 : 0u);
+    const auto rv = make_rsrc(static_cast<const char*>(a.v) + off0, store_span(a, kt, rstride, kHeadDim * 2));
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
@@ -196,8 +204,8 @@ __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk
   } else {
     constexpr int G = MODE == 2 ? 4 : 1;  // scales per row
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
-    const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, rows * kHeadDim);
-    const auto rvs = make_rsrc(a.v_scale + hrow * G, rows * 2 * G);
+    const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, store_span(a, kt, kHeadDim, kHeadDim));
+    const auto rvs = make_rsrc(a.v_scale + hrow * G, store_span(a, kt, 2 * G, 2 * G));
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int u = tid + NT * j;
