@@ -91,7 +91,8 @@ def test_outlier16k_sampled_rows(mode):
 
 
 @pytest.mark.parametrize("mode", ["exact", "kvi8r"])
-@pytest.mark.parametrize("s_q,s_kv,heads,q_chunk", [(1000, 777, 3, 300), (65, 1, 2, 64), (257, 129, 1, 1000)])
+@pytest.mark.parametrize("s_q,s_kv,heads,q_chunk", [(1000, 777, 3, 300), (65, 1, 2, 64), (257, 129, 1, 1000),
+                                                     (130, 200, 96, 64)])  # wide token stride, ragged last tile
 def test_ragged_shapes(mode, s_q, s_kv, heads, q_chunk):
     w = synth.Workload("ragged", max(s_q, s_kv), heads, 7, q_chunk, 0)
     full = synth.qkv_bf16(w)
