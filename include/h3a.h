@@ -80,8 +80,11 @@ const char* h3a_last_error(void);
  *     entries +-1/sqrt(128));
  *   scale = fp16(max|y| / 127), rounded to nearest-even from the exact value;
  *     0 for a zero row; saturates at 65504;
- *   code_i = clamp(round-half-even(y_i / scale), -127, 127) as int8, taken in
- *     fp32 against the stored (rounded) scale.
+ *   code_i = clamp(round-half-even(y_i / scale), -127, 127) as int8, against
+ *     the stored (rounded) scale.  y_i / scale is evaluated in fp32 (butterflies,
+ *     then one product with an fp32 reciprocal of the scale), so where it lies
+ *     within that evaluation's rounding error of a half-step (about 1e-4 of a
+ *     step for Gaussian rows) the code may be either neighbour.
  *
  * x:               bf16 [n_tokens, n_heads, 128]; token t, head h starts at
  *                  element t * x_token_stride + h * 128.  16-byte aligned.

@@ -9,20 +9,19 @@ It is plain and slow on purpose: explicit matrices instead of butterflies,
 fp64 NumPy throughout, per-head processing.  What it follows:
 
 * "H3 Streamed Blocks (exact low-VRAM, alpha)" node page, Inputs table,
-  kv_store row: K and V held as int8 with one fp16 scale per (token, head) row
-  in a fixed orthonormal 128-wide Hadamard-rotated basis; the query chunk is
-  rotated to match and the output un-rotated once; a block dequant is one
-  int8 -> fp16 cast times the scale; attention runs blockwise (kv_block) with an
-  online-softmax combine.  Same row: q_chunk "exact at any value".
+  kv_store row (the kvi8r store: a Hadamard rotation of each K/V row, int8
+  codes, an fp16 scale per row, dequantisation per block, blockwise attention
+  with a softmax combine across blocks, the query rotated in and the output
+  rotated out) and q_chunk row (the result does not depend on the chunking).
 * "Low VRAM, low RAM: the de-rope on a 16 GB card" page, "The K/V store
-  options": scores are invariant under the rotation, P.V is brought back
-  through the transpose once; fp16 rather than bf16 inside kvi8r.  "What is
-  next": a kvi8r variant with one scale per 32 values.
+  options" (why rotating both sides leaves the scores unchanged, and the fp16
+  precision inside kvi8r) and "What is next" (the one-scale-per-32-values
+  variant).
 * "H3-Optimizations" page, Nodes (H3 Sparse Attention and the routed-geometry
-  paragraph): 64Q x 64KV tiles, the hard arm drops rejected tiles, the Sol arm
-  stands in for them with block-mean K and block-sum V.
-* Node page, Inputs table, exact_av_rows row: chosen query rows attend a bf16
-  K/V exactly while the rest use the quantised store.
+  paragraph): 64Q x 64KV tiles, a hard arm that leaves rejected tiles out and a
+  Sol arm that summarises them.
+* Node page, Inputs table, exact_av_rows row: a per-row choice between exact
+  attention over a bf16 K/V and the quantised store.
 
 Modules: ``hadamard`` (the basis), ``encodings`` (exact bf16/fp16 decoding and
 fp16 rounding), ``kvi8r`` (quantise / dequantise), ``attention`` (exact, kvi8r,
@@ -36,7 +35,8 @@ routine; none is "parity unpinned".
 """
 from .hadamard import sylvester_hadamard, orthonormal_hadamard
 from .encodings import bf16_to_f64, f16_to_f64, f64_to_f16_bits
-from .kvi8r import (rotate_rows, row_scales, codes_for_scales, quantize_rows, dequantize_rows,
+from .kvi8r import (rotate_rows, row_scales, codes_for_scales, fp32_decision_width, near_ties, quantize_rows,
+                    dequantize_rows,
                     quantize_rows_grouped, dequantize_rows_grouped)
 from .attention import (attention, attention_blockwise, kvi8r_attention, expand_tile_mask,
                         exact_attention_bf16)
@@ -45,7 +45,8 @@ from .routing import spans_to_rows, routed_attention
 
 __all__ = [
     "sylvester_hadamard", "orthonormal_hadamard", "bf16_to_f64", "f16_to_f64", "f64_to_f16_bits",
-    "rotate_rows", "row_scales", "codes_for_scales", "quantize_rows", "dequantize_rows",
+    "rotate_rows", "row_scales", "codes_for_scales", "fp32_decision_width", "near_ties", "quantize_rows",
+    "dequantize_rows",
     "quantize_rows_grouped", "dequantize_rows_grouped",
     "attention", "attention_blockwise", "kvi8r_attention", "expand_tile_mask",
     "tile_summaries", "sol_attention", "exact_sol_attention_bf16", "kvi8r_sol_attention",

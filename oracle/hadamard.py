@@ -1,10 +1,11 @@
 """The fixed orthonormal 128-wide Hadamard basis (oracle; test infrastructure only).
 
-Pages: "H3 Streamed Blocks" node page, Inputs table, kv_store row ("a fixed
-orthonormal 128-wide Hadamard-rotated basis of the head dim"); "Low VRAM, low
-RAM" page, "The K/V store options", rotation paragraph.  The pages name neither
-construction, ordering nor sign pattern; the reading taken here is Sylvester's
-construction in natural order with no sign flips, scaled by 1/sqrt(128).
+Cited: "H3 Streamed Blocks" node page, Inputs table, kv_store row, and the
+"Low VRAM, low RAM" page, "The K/V store options", rotation paragraph.  Both
+call for one fixed orthonormal Hadamard rotation of width 128 over the head
+dimension, and neither says how the matrix is built, ordered or signed.  The
+reading taken here: Sylvester's doubling construction in natural order, no
+sign flips, scaled by 1/sqrt(128).
 """
 from __future__ import annotations
 

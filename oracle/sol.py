@@ -1,9 +1,10 @@
 """Tile-masked attention with a residual for the dropped tiles (oracle; test infrastructure only).
 
-"H3-Optimizations" page, Nodes, routed-geometry paragraph: besides the hard arm,
-which drops rejected 64Q x 64KV tiles, a Sol arm stands in for each rejected
-tile with its block-mean K and block-sum V and merges that residual into the
-kernel's softmax state.  Reading taken here (the page gives no formula):
+Cited: "H3-Optimizations" page, Nodes, routed-geometry paragraph.  Two arms
+are described there: the hard arm leaves rejected 64Q x 64KV tiles out of the
+softmax; the Sol arm keeps a summary of each rejected tile (the mean of its
+keys, the sum of its values) and folds that into the online-softmax state.  No
+formula is given; the reading taken here:
 
 * a dropped KV tile t with n_t keys (64, or fewer for the last tile of the
   store) becomes one pseudo-key: k_t = mean of its keys, value v_t = mean of its
