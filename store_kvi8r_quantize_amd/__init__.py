@@ -101,10 +101,30 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _stream_obj(t, stream):
+    """The torch stream the call's work is queued on: the caller's (a torch stream, or a raw hipStream_t
+    handle wrapped as an external stream), else the current stream of t's device."""
+    if stream is None:
+        return torch.cuda.current_stream(t.device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=t.device)
+
+
 def _stream(t, stream):
-    if stream is not None:
-        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
-    return torch.cuda.current_stream(t.device).cuda_stream
+    return _stream_obj(t, stream).cuda_stream
+
+
+def _workspace(need: int, device, stream_obj):
+    """A workspace of `need` bytes for work queued on stream_obj.
+
+    It is allocated with stream_obj current, so the caching allocator files the
+    block under that stream: when the tensor is freed (on return), the block is
+    handed out again only to work ordered after what is already queued on that
+    stream, which includes the kernels that use it.
+    """
+    with torch.cuda.stream(stream_obj):
+        return torch.empty(need, dtype=torch.uint8, device=device)
 
 
 def _need(t, name, dtype):
@@ -199,12 +219,13 @@ def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: i
         softmax_scale = 1.0 / math.sqrt(head_dim)
     need = int(lib.h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, int(mode) | flags,
                                                  int(tile_mask is not None)))
+    st = _stream_obj(q, stream)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, st)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.h3a_attention(_ptr(q), _ptr(k_store), _ptr(v_store), _ptr(scales), s_q, s_kv, n_heads, head_dim,
                              float(softmax_scale), int(q_chunk), int(kv_block), int(mode) | flags, _ptr(tile_mask),
-                             _ptr(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
+                             _ptr(out), _ptr(workspace), ws_bytes, st.cuda_stream))
     return out
 
 
@@ -239,12 +260,13 @@ def h3a_attention_routed(q, k_bf16, v_bf16, store, out, *, exact_spans, q_chunk:
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
     need = int(lib.h3a_attention_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, MODE_KVI8R, 0))
+    st = _stream_obj(q, stream)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, st)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.h3a_attention_routed(_ptr(q), _ptr(k_bf16), _ptr(v_bf16), _ptr(kc), _ptr(vc), _ptr(sc), s_q, s_kv,
                                     n_heads, head_dim, float(softmax_scale), int(q_chunk), int(kv_block), spans,
-                                    len(flat) // 2, _ptr(out), _ptr(workspace), ws_bytes, _stream(q, stream)))
+                                    len(flat) // 2, _ptr(out), _ptr(workspace), ws_bytes, st.cuda_stream))
     return out
 
 
@@ -279,13 +301,14 @@ def h3a_attention_host_kv(q, k_host, v_host, scales_host, out, *, q_chunk: int, 
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(head_dim)
     need = int(lib.h3a_attention_host_kv_workspace_bytes(s_q, s_kv, n_heads, head_dim, q_chunk, kv_block, int(mode)))
+    st = _stream_obj(q, stream)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(need, q.device, st)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     hp = lambda t: None if t is None else t.data_ptr()
     _check(lib.h3a_attention_host_kv(_ptr(q), hp(k_host), hp(v_host), hp(scales_host), s_q, s_kv, n_heads, head_dim,
                                      float(softmax_scale), int(q_chunk), int(kv_block), int(mode), _ptr(out),
-                                     _ptr(workspace), ws_bytes, _stream(q, stream)))
+                                     _ptr(workspace), ws_bytes, st.cuda_stream))
     return out
 
 

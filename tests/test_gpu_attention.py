@@ -206,3 +206,26 @@ def test_long217k_sampled_rows(mode):
     def rows(h):
         return synth.sampled_rows(w, h, w.oracle_rows_per_head if h in full else 64)
     _check(mode, range(w.heads), bits, out, store, rows, tag="long217k")
+
+
+@pytest.mark.parametrize("raw_handle", [False, True])
+def test_side_stream_with_binding_workspace(raw_handle):
+    # The binding allocates the workspace (workspace=None) for kernels queued on a side stream, then the
+    # current stream immediately allocates and fills memory of the same size.  The workspace belongs to the
+    # side stream's pool, so that churn cannot take its block while the kernels run: the output is bitwise
+    # that of the same call on the current stream.
+    w, bits, g = _inputs("outlier16k")
+    store = build_store(g["k"], g["v"])
+    ref = _run("kvi8r", g["q"], g["k"], g["v"], store, q_chunk=4096)
+    need = h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, 4096, "kvi8r", False)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out = torch.empty_like(g["q"])
+    for _ in range(3):
+        h3a.h3a_attention(g["q"], *store, out, q_chunk=4096, mode="kvi8r",
+                          stream=side.cuda_stream if raw_handle else side)
+        junk = [torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda") for _ in range(2)]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
