@@ -15,7 +15,7 @@ routing at a 30 % video-KV budget with the text prefix kept dense
 Random streams: every (tensor, head) pair has its own PCG64 stream seeded with
 SeedSequence([seed, stream, head]) so any single head can be regenerated alone.
 Streams: 0 = Q, 1 = K, 2 = V, 3 = outlier channels of K, 4 = tile mask,
-5 = sampled query rows.
+5 = sampled query rows, 6 = sampled video query tiles.
 """
 from __future__ import annotations
 
@@ -28,7 +28,7 @@ import numpy as np
 HEAD_DIM = 128
 TILE = 64
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_OUTLIER, STREAM_MASK, STREAM_ROWS = 0, 1, 2, 3, 4, 5
+STREAM_Q, STREAM_K, STREAM_V, STREAM_OUTLIER, STREAM_MASK, STREAM_ROWS, STREAM_QTILES = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclass(frozen=True)
@@ -182,3 +182,18 @@ def tile_mask(w: Workload) -> np.ndarray:
         for qt in range(text, nt):
             mask[h, qt, text + rng.choice(n_video, size=keep, replace=False)] = 1
     return mask
+
+
+def sampled_q_tiles(w: Workload, head: int, n_video: int = 24) -> np.ndarray:
+    """Sorted 64-row query tiles of one head for an oracle sample of a tile-masked workload: every
+    text-prefix tile plus n_video video tiles drawn without replacement from the head's stream."""
+    text = (w.text_prefix + TILE - 1) // TILE
+    n_vid = w.n_tiles - text
+    video = text + _rng(w.seed, STREAM_QTILES, head).choice(n_vid, size=min(n_video, n_vid), replace=False)
+    return np.sort(np.concatenate([np.arange(text), video]))
+
+
+def q_tile_rows(w: Workload, tiles: np.ndarray) -> np.ndarray:
+    """Query rows of the given 64-row tiles, clipped to the sequence."""
+    rows = (np.asarray(tiles)[:, None] * TILE + np.arange(TILE)[None, :]).reshape(-1)
+    return rows[rows < w.seq]

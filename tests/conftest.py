@@ -8,3 +8,18 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+try:
+    import pytest
+
+    @pytest.fixture(scope="session")
+    def oracle_pool():
+        """Processes for fp64 oracle jobs at the workloads' stated sample sizes (one head per job)."""
+        from parity import OraclePool
+
+        pool = OraclePool()
+        yield pool
+        pool.close()
+except ImportError:  # pragma: no cover
+    pass

@@ -11,16 +11,8 @@ import oracle
 import store_kvi8r_quantize_amd as h3a
 import synth
 
-SCALE = 1.0 / math.sqrt(128.0)
-
-# Tolerances stated for this path: kvi8r output against the oracle on the same
-# dequantised K/V: relative L2 <= 2e-3 and max abs <= 1e-2; exact path against
-# the unquantised inputs: relative L2 <= 4e-3.  Codes: <= 1e-4 off by one (ties);
-# scales within 1 fp16 ulp.
-KVI8R_REL_L2 = 2e-3
-KVI8R_MAX_ABS = 1e-2
-EXACT_REL_L2 = 4e-3
-CODE_MISMATCH = 1e-4
+from parity import (CODE_MISMATCH, EXACT_REL_L2, KVI8R_MAX_ABS, KVI8R_REL_L2, SCALE,  # noqa: F401 (re-exported)
+                    assert_quantize_ok, quantize_report, rel_l2)
 
 
 def say(*a):
@@ -34,12 +26,6 @@ def gpu_u16(a: np.ndarray, dtype=torch.bfloat16) -> torch.Tensor:
 
 def host_u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
-
-
-def rel_l2(got, ref) -> float:
-    d = np.linalg.norm(np.asarray(got, np.float64) - ref)
-    n = np.linalg.norm(ref)
-    return float(d / n) if n > 0 else float(d)
 
 
 def gpu_inputs(w: synth.Workload, tensors=("q", "k", "v")) -> dict:
@@ -89,51 +75,6 @@ def build_store(k: torch.Tensor, v: torch.Tensor, kv_chunk: int | None = None):
     return kc, vc, sc
 
 
-def quantize_report(x_bits: np.ndarray, codes_gpu: np.ndarray, scale_bits_gpu: np.ndarray, group: int = 128) -> dict:
-    """Compare one head's GPU codes and scales with the oracle.
-
-    x_bits: bf16 bits [n, 128]; codes_gpu: int8 [n, 128]; scale_bits_gpu: [n] (one scale per row) or
-    [n, 4] (group = 32).  Codes are compared with the oracle's codes taken on the GPU's scales (so that
-    a scale one ulp off is judged on its own), and with the oracle's own codes.  A differing code is
-    allowed only where y / s lies inside the fp32 near-tie band (oracle.fp32_decision_width) and only
-    by one step; the rate of differences is capped separately.
-    """
-    x = oracle.bf16_to_f64(x_bits)
-    n = x.shape[0]
-    if group == 128:
-        codes_o, s_o, y = oracle.quantize_rows(x)
-    else:
-        codes_o, s_o, y = oracle.quantize_rows_grouped(x, group)
-    sg = np.asarray(scale_bits_gpu, dtype=np.uint16).reshape(s_o.shape)
-    yg = y.reshape(-1, group)
-    sg_flat = sg.reshape(-1)
-    at_gpu = oracle.codes_for_scales(yg, sg_flat).reshape(n, 128)
-    ties = oracle.near_ties(yg, sg_flat, oracle.fp32_decision_width(x, sg, group).reshape(-1, group)).reshape(n, 128)
-    got = np.asarray(codes_gpu).astype(np.int64)
-    d_same = got - at_gpu
-    d_own = got - codes_o
-    off = d_same != 0
-    return {
-        "rows": n,
-        "scale_max_ulp": int(np.abs(sg.astype(np.int64) - s_o.astype(np.int64)).max()) if n else 0,
-        "scale_rows_differ": int(np.count_nonzero(sg != s_o)),
-        "code_mismatch_frac": float(np.count_nonzero(d_own) / max(d_own.size, 1)),
-        "code_mismatch_same_scale": int(np.count_nonzero(off)),
-        "code_mismatch_same_scale_frac": float(np.count_nonzero(off) / max(off.size, 1)),
-        "code_max_diff_same_scale": int(np.abs(d_same).max()) if d_same.size else 0,
-        "code_mismatch_off_tie": int(np.count_nonzero(off & ~ties)),
-        "near_tie_frac": float(ties.mean()) if ties.size else 0.0,
-    }
-
-
-def assert_quantize_ok(rep: dict):
-    assert rep["scale_max_ulp"] <= 1, rep
-    assert rep["code_mismatch_off_tie"] == 0, rep  # every differing code sits at a near-tie
-    assert rep["code_max_diff_same_scale"] <= 1, rep
-    assert rep["code_mismatch_same_scale_frac"] <= CODE_MISMATCH, rep
-    assert rep["code_mismatch_frac"] <= CODE_MISMATCH, rep
-
-
 def store_head(kc, vc, sc, h):
     """Host copies of one head of a kvi8r store: (k codes, k scale bits, v codes, v scale bits)."""
     return (kc[h].cpu().numpy(), host_u16(sc[0, h]), vc[h].cpu().numpy(), host_u16(sc[1, h]))
@@ -154,3 +95,31 @@ def oracle_kvi8r_rows(src: HeadSource, store_h, h, rows, mask=None):
 
 def out_rows(out_gpu_bits: np.ndarray, h, rows) -> np.ndarray:
     return oracle.bf16_to_f64(out_gpu_bits[rows, h])
+
+
+def pool_check(pool, kind, w, out, heads, rows_of, store=None, mask=None, tag="", s_kv=None):
+    """Compare GPU output rows with the fp64 oracle, one head per pool job, gates per head and pooled.
+
+    kind: "exact", "kvi8r", "sol_exact" or "sol_kvi8r"; store: the GPU's kvi8r store (k codes, v codes,
+    scales) for kvi8r kinds; mask: the tile mask [H, nQt, nKt] for masked kinds.
+    """
+    from parity import assert_attention_ok, attention_job
+
+    specs = []
+    for h in heads:
+        rows = np.asarray(rows_of(h))
+        spec = {"kind": kind, "workload": w, "head": h, "rows": rows, "s_kv": s_kv,
+                "got": host_u16(out[torch.from_numpy(rows).cuda(), h])}
+        if store is not None:
+            spec["store"] = store_head(*store, h)
+        if mask is not None:
+            spec["mask"] = np.ascontiguousarray(mask[h])
+        specs.append(spec)
+    results = []
+    for r in pool.ex.map(attention_job, specs):
+        say(tag, kind, "head", r["head"], "rows", r["rows"], "relL2", r["rel_l2"], "max abs", r["max_abs"])
+        results.append(r)
+    gate = {"sol_exact": "exact", "sol_kvi8r": "kvi8r"}.get(kind, kind)
+    summary = assert_attention_ok(results, gate)
+    say(tag, kind, "summary", summary)
+    return summary

@@ -140,22 +140,18 @@ def test_sol_all_kept_equals_dense_bitwise(mode):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("mode", ["kvi8r", "exact"])
-def test_sol_sparse64k_sampled_rows(mode):
-    from gpu_common import HeadSource, gpu_inputs
+def test_sol_sparse64k_oracle_sample(mode, oracle_pool):
+    # every text q-tile (8) plus 24 seeded video q-tiles of each of the 32 heads: 2048 rows per head
+    from gpu_common import gpu_inputs, pool_check
 
     w = synth.WORKLOADS["sparse64k"]
     say("generating", w.name)
     g = gpu_inputs(w)
-    src = HeadSource(w)
     mask = synth.tile_mask(w)
     store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk) if mode == "kvi8r" else None
     out = _run(mode, g["q"], g["k"], g["v"], store, w.q_chunk, torch.from_numpy(mask).cuda())
-    got, ref = [], []
-    for h in range(1, w.heads, 8):
-        rows = np.unique(np.concatenate([np.arange(0, 512, 32), synth.sampled_rows(w, h, 64)]))
-        got.append(_rows_out(out, rows, h))
-        ref.append(_sol_ref(mode, src, store, h, rows, mask[h]))
-    _assert_close(mode, np.concatenate(got), np.concatenate(ref), "sol-sparse64k")
+    pool_check(oracle_pool, "sol_" + mode, w, out, range(w.heads),
+               lambda h: synth.q_tile_rows(w, synth.sampled_q_tiles(w, h)), store, mask=mask, tag="sol-sparse64k")
 
 
 @pytest.mark.parametrize("mode", ["exact", "kvi8r"])

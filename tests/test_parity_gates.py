@@ -55,3 +55,33 @@ def test_scale_two_ulps_off_fails():
     bad[5] += 2
     with pytest.raises(AssertionError):
         assert_quantize_ok(quantize_report(bits, codes, bad))
+
+
+def _bf16_bits(a):
+    return synth.bf16_bits_from_f32(np.asarray(a, np.float32))
+
+
+def test_oracle_pool_jobs_and_per_head_gate():
+    # Spawned workers regenerate each head's inputs and return error statistics.  The "GPU" rows here are
+    # the oracle's own output rounded to bf16, so every head passes; rows of another head fail that head.
+    from parity import OraclePool, assert_attention_ok, attention_job, quantize_job, reference_rows
+
+    w = synth.WORKLOADS["tiny"]
+    rows = synth.sampled_rows(w, 0, 64)
+    good = [_bf16_bits(reference_rows("exact", w, h, rows)) for h in range(w.heads)]
+    specs = [{"kind": "exact", "workload": w, "head": h, "rows": rows, "got": good[h]} for h in range(w.heads)]
+    pool = OraclePool(2)
+    try:
+        res = pool.map(attention_job, specs)
+        s = assert_attention_ok(res, "exact")
+        assert s["rows"] == 64 * w.heads and 0 < s["rel_l2"] < 2e-3
+        specs[1]["got"] = good[0]
+        with pytest.raises(AssertionError):
+            assert_attention_ok(pool.map(attention_job, specs), "exact")
+        x = synth.head_bf16(w, "k", 1)
+        codes, s_bits, _ = oracle.quantize_rows(oracle.bf16_to_f64(x))
+        rep = pool.map(quantize_job, [{"workload": w, "tensor": "k", "head": 1, "codes": codes, "scales": s_bits}])[0]
+        assert_quantize_ok(rep)
+        assert rep["code_mismatch_same_scale"] == 0 and rep["head"] == 1
+    finally:
+        pool.close()
