@@ -182,6 +182,36 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
                       void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * h3a_attention_noalloc -- h3a_attention for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * Same arguments, checks, kernels and results as h3a_attention (bitwise), with
+ * no workspace argument: the scratch it needs (rotated query chunk, rotated
+ * output, tile lists, tile means) lives in a device array inside the library,
+ * H3A_NOALLOC_SCRATCH_BYTES bytes on every GPU it runs on, held until the
+ * process ends.  The call makes no hipMalloc / hipFree and calls no allocating
+ * routine.  The caller still owns q, the store, tile_mask and out.
+ *
+ * A call whose h3a_attention_workspace_bytes(...) exceeds
+ * H3A_NOALLOC_SCRATCH_BYTES returns H3A_EWORKSPACE and queues nothing.  The
+ * output does not depend on q_chunk, so a smaller q_chunk gives the same
+ * result with less scratch (kvi8r modes need 768 bytes per query row and
+ * head of a chunk: q_chunk 8192 at 32 heads fits).
+ *
+ * Every call on one GPU uses that GPU's one array, which keeps whatever the
+ * last call left there; every kernel writes the scratch it reads within the
+ * same call, so nothing needs clearing.  Calls that overlap on one GPU (queued
+ * on different streams without ordering between them) race on the array: order
+ * them on one stream, or use h3a_attention with a workspace each.
+ */
+#define H3A_NOALLOC_SCRATCH_BYTES (256u << 20) /* 256 MiB per GPU */
+int32_t h3a_attention_noalloc(const void* q, const void* k_store, const void* v_store, const void* scales,
+                              int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                              int64_t q_chunk, int64_t kv_block, int32_t mode, const uint8_t* tile_mask,
+                              void* out, void* stream);
+
+/*
  * h3a_attention_routed -- h3a_attention over two stores of the same K/V, chosen
  * per query row [P1 Inputs table, exact_av_rows row: text and audio rows attend
  * a retained bf16 K/V exactly, the other rows the quantised store].

@@ -8,7 +8,7 @@ There is no CPU fallback: if the library is not built, or its ABI version does
 not match, every call raises.
 
 Functions carry the C names: h3a_kv_quantize (+ h3a_kv_quantize_g32, chosen by the
-scales' shape), h3a_attention, h3a_attention_routed, h3a_attention_host_kv
+scales' shape), h3a_attention, h3a_attention_noalloc, h3a_attention_routed, h3a_attention_host_kv
 (+ its workspace query),
 h3a_attention_workspace_bytes, h3a_rotate_rows, h3a_unrotate_rows,
 h3a_timing_enable, h3a_timing_collect, h3a_abi_version.
@@ -29,6 +29,7 @@ MODE_KVI8R = 1
 MODE_KVI8R32 = 2  # kvi8r with one fp16 scale per 32 rotated values
 MODES = {"exact": MODE_EXACT_BF16, "bf16": MODE_EXACT_BF16, "kvi8r": MODE_KVI8R, "kvi8r32": MODE_KVI8R32}
 SOL = 0x100  # H3A_SOL: dropped tiles of a tile_mask enter as one pseudo-key each
+NOALLOC_SCRATCH_BYTES = 256 << 20  # H3A_NOALLOC_SCRATCH_BYTES: the library's own scratch per GPU
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libh3a.so")
 
@@ -66,6 +67,8 @@ def _load():
     lib.h3a_attention_workspace_bytes.argtypes = [i64, i64, i32, i32, i64, i32, i32]
     lib.h3a_attention.restype = i32
     lib.h3a_attention.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64, i32, vp, vp, vp, sz, vp]
+    lib.h3a_attention_noalloc.restype = i32
+    lib.h3a_attention_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64, i32, vp, vp, vp]
     lib.h3a_attention_routed.restype = i32
     lib.h3a_attention_routed.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, f32, i64, i64,
                                          ctypes.POINTER(ctypes.c_int64), i32, vp, vp, sz, vp]
@@ -226,6 +229,42 @@ def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: i
     _check(lib.h3a_attention(_ptr(q), _ptr(k_store), _ptr(v_store), _ptr(scales), s_q, s_kv, n_heads, head_dim,
                              float(softmax_scale), int(q_chunk), int(kv_block), int(mode) | flags, _ptr(tile_mask),
                              _ptr(out), _ptr(workspace), ws_bytes, st.cuda_stream))
+    return out
+
+
+def h3a_attention_noalloc(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: int = 0, mode="kvi8r",
+                          tile_mask=None, sol: bool = False, softmax_scale: float | None = None, stream=None):
+    """h3a_attention without a workspace: the library's own per-GPU scratch (NOALLOC_SCRATCH_BYTES) is used,
+    and nothing is allocated, here or in the library.  A call needing more scratch raises H3AError
+    (H3A_EWORKSPACE); a smaller q_chunk needs less and gives the same output.  Calls on one GPU share the
+    scratch, so calls on different streams must not overlap."""
+    lib = _load()
+    mode = MODES.get(mode, mode)
+    flags = SOL if sol else 0
+    _need(q, "q", torch.bfloat16)
+    _need(out, "out", torch.bfloat16)
+    if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
+        raise ValueError("q and out must be contiguous [s_q, n_heads, head_dim] tensors of equal shape")
+    s_q, n_heads, head_dim = q.shape
+    if mode in (MODE_KVI8R, MODE_KVI8R32):
+        _need(k_store, "k_store", torch.int8)
+        _need(v_store, "v_store", torch.int8)
+        _need(scales, "scales", torch.float16)
+        s_kv = k_store.shape[1]
+    else:
+        _need(k_store, "k_store", torch.bfloat16)
+        _need(v_store, "v_store", torch.bfloat16)
+        s_kv = k_store.shape[0]
+    for name, t in (("k_store", k_store), ("v_store", v_store), ("scales", scales), ("tile_mask", tile_mask)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tile_mask is not None:
+        _need(tile_mask, "tile_mask", torch.uint8)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(head_dim)
+    _check(lib.h3a_attention_noalloc(_ptr(q), _ptr(k_store), _ptr(v_store), _ptr(scales), s_q, s_kv, n_heads,
+                                     head_dim, float(softmax_scale), int(q_chunk), int(kv_block), int(mode) | flags,
+                                     _ptr(tile_mask), _ptr(out), _stream(q, stream)))
     return out
 
 

@@ -16,6 +16,13 @@
 #include "h3a.h"
 #include "launch.h"
 
+// Scratch of h3a_attention_noalloc: one file-scope device array; every GPU the
+// library runs on holds its own copy for the life of the process.  In host code
+// `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current
+// (scratch_address below), and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[H3A_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
@@ -425,6 +432,92 @@ int kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t
                                             grouped, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3A_OK : hip_fail(e, "kvi8r_quantize launch");
 }
+
+// ---- scratch of h3a_attention_noalloc --------------------------------------------------
+std::mutex g_scratch_mu;
+std::vector<std::pair<int, char*>> g_scratch;  // (device, address of that device's copy of `scratch`)
+
+int scratch_address(char** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  for (auto& p : g_scratch)
+    if (p.first == dev) {
+      *out = p.second;
+      return H3A_OK;
+    }
+  void* ptr = nullptr;
+  if ((e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) != hipSuccess)
+    return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  if (ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0)
+    return fail(H3A_EHIP, "scratch: device address %p is not 256-byte aligned", ptr);
+  g_scratch.emplace_back(dev, static_cast<char*>(ptr));
+  *out = static_cast<char*>(ptr);
+  return H3A_OK;
+}
+
+// h3a_attention and h3a_attention_noalloc: the same checks and the same query-chunk
+// loop; the second takes its workspace from `scratch` instead of the caller.
+int attention_call(const void* q, const void* k_store, const void* v_store, const void* scales, int64_t s_q,
+                   int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale, int64_t q_chunk,
+                   int64_t kv_block, int32_t mode, const uint8_t* tile_mask, void* out, void* workspace,
+                   size_t workspace_bytes, bool use_scratch, void* stream) {
+  g_err.clear();
+  if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  const bool sol = (mode & H3A_SOL) != 0;
+  const int32_t mode_arg = mode;
+  mode &= ~H3A_SOL;
+  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32)
+    return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
+  if (sol && tile_mask == nullptr) return fail(H3A_EINVAL, "H3A_SOL needs a tile_mask");
+  if (sol && s_kv > h3a::kSolMaxKv) return fail(H3A_EINVAL, "H3A_SOL supports s_kv up to 2^30 - 64");
+  int rc;
+  if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
+  const bool sparse = tile_mask != nullptr;
+  if (sparse && q_chunk % H3A_TILE != 0)
+    return fail(H3A_EINVAL, "q_chunk must be a multiple of 64 with a tile_mask (got %lld)", (long long)q_chunk);
+  if (mode != H3A_MODE_EXACT_BF16 && scales == nullptr && s_kv > 0)
+    return fail(H3A_EINVAL, "kvi8r modes need scales");
+  if (mode == H3A_MODE_EXACT_BF16 && scales != nullptr) return fail(H3A_EINVAL, "exact mode takes no scales");
+  WorkspaceLayout wl;
+  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse, sol, &wl))
+    return fail(H3A_EINVAL, "size overflow");
+  if (use_scratch && wl.total > (uint64_t)H3A_NOALLOC_SCRATCH_BYTES)
+    return fail(H3A_EWORKSPACE,
+                "h3a_attention_noalloc: this call needs %llu bytes of scratch, more than its %llu; a smaller "
+                "q_chunk needs less and gives the same output",
+                (unsigned long long)wl.total, (unsigned long long)H3A_NOALLOC_SCRATCH_BYTES);
+  if (s_q == 0) return H3A_OK;
+
+  if ((rc = check_rows(q, out, s_q, n_heads)) != H3A_OK) return rc;
+  if ((rc = check_store(mode, k_store, v_store, scales, s_kv, n_heads, "k_store", "v_store")) != H3A_OK) return rc;
+  const int64_t n_qt_total = (s_q + H3A_TILE - 1) / H3A_TILE, n_kt = (s_kv + H3A_TILE - 1) / H3A_TILE;
+  if (sparse) {
+    int64_t mb;
+    if (!mul_ok(n_qt_total * n_heads, n_kt, &mb)) return fail(H3A_EINVAL, "tile_mask size overflow");
+    if ((rc = check_buffer(tile_mask, (uint64_t)mb, 1, "tile_mask")) != H3A_OK) return rc;
+  }
+  char* ws = static_cast<char*>(workspace);
+  if (use_scratch) {
+    if (wl.total > 0 && (rc = scratch_address(&ws)) != H3A_OK) return rc;
+  } else if ((rc = check_workspace(workspace, workspace_bytes, wl)) != H3A_OK) {
+    return rc;
+  }
+
+  Pass p = make_pass(mode, q, out, k_store, v_store, scales, s_q, s_kv, n_heads, softmax_scale, q_chunk, ws, wl,
+                     stream);
+  p.tile_mask = tile_mask;
+  p.sol = sol;
+  if (sol) {
+    hipError_t e = h3a::launch_tile_means(mode, k_store, v_store, p.k_scale, p.v_scale, s_kv, n_heads,
+                                          reinterpret_cast<uint16_t*>(p.ws + wl.kmean),
+                                          reinterpret_cast<uint16_t*>(p.ws + wl.vmean),
+                                          reinterpret_cast<float*>(p.ws + wl.kmscale), p.st);
+    if (e != hipSuccess) return hip_fail(e, "tile_means launch");
+  }
+  return attend_rows(p, 0, s_q);
+}
 }  // namespace
 
 extern "C" {
@@ -462,50 +555,16 @@ int32_t h3a_attention(const void* q, const void* k_store, const void* v_store, c
                       int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale, int64_t q_chunk,
                       int64_t kv_block, int32_t mode, const uint8_t* tile_mask, void* out, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
-  const bool sol = (mode & H3A_SOL) != 0;
-  const int32_t mode_arg = mode;
-  mode &= ~H3A_SOL;
-  if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32)
-    return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
-  if (sol && tile_mask == nullptr) return fail(H3A_EINVAL, "H3A_SOL needs a tile_mask");
-  if (sol && s_kv > h3a::kSolMaxKv) return fail(H3A_EINVAL, "H3A_SOL supports s_kv up to 2^30 - 64");
-  int rc;
-  if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
-  const bool sparse = tile_mask != nullptr;
-  if (sparse && q_chunk % H3A_TILE != 0)
-    return fail(H3A_EINVAL, "q_chunk must be a multiple of 64 with a tile_mask (got %lld)", (long long)q_chunk);
-  if (mode != H3A_MODE_EXACT_BF16 && scales == nullptr && s_kv > 0)
-    return fail(H3A_EINVAL, "kvi8r modes need scales");
-  if (mode == H3A_MODE_EXACT_BF16 && scales != nullptr) return fail(H3A_EINVAL, "exact mode takes no scales");
-  if (s_q == 0) return H3A_OK;
+  return attention_call(q, k_store, v_store, scales, s_q, s_kv, n_heads, head_dim, softmax_scale, q_chunk, kv_block,
+                        mode, tile_mask, out, workspace, workspace_bytes, false, stream);
+}
 
-  if ((rc = check_rows(q, out, s_q, n_heads)) != H3A_OK) return rc;
-  if ((rc = check_store(mode, k_store, v_store, scales, s_kv, n_heads, "k_store", "v_store")) != H3A_OK) return rc;
-  const int64_t n_qt_total = (s_q + H3A_TILE - 1) / H3A_TILE, n_kt = (s_kv + H3A_TILE - 1) / H3A_TILE;
-  if (sparse) {
-    int64_t mb;
-    if (!mul_ok(n_qt_total * n_heads, n_kt, &mb)) return fail(H3A_EINVAL, "tile_mask size overflow");
-    if ((rc = check_buffer(tile_mask, (uint64_t)mb, 1, "tile_mask")) != H3A_OK) return rc;
-  }
-  WorkspaceLayout wl;
-  if (!workspace_layout(s_q, s_kv, n_heads, q_chunk, mode, sparse, sol, &wl))
-    return fail(H3A_EINVAL, "size overflow");
-  if ((rc = check_workspace(workspace, workspace_bytes, wl)) != H3A_OK) return rc;
-
-  Pass p = make_pass(mode, q, out, k_store, v_store, scales, s_q, s_kv, n_heads, softmax_scale, q_chunk,
-                     static_cast<char*>(workspace), wl, stream);
-  p.tile_mask = tile_mask;
-  p.sol = sol;
-  if (sol) {
-    hipError_t e = h3a::launch_tile_means(mode, k_store, v_store, p.k_scale, p.v_scale, s_kv, n_heads,
-                                          reinterpret_cast<uint16_t*>(p.ws + wl.kmean),
-                                          reinterpret_cast<uint16_t*>(p.ws + wl.vmean),
-                                          reinterpret_cast<float*>(p.ws + wl.kmscale), p.st);
-    if (e != hipSuccess) return hip_fail(e, "tile_means launch");
-  }
-  return attend_rows(p, 0, s_q);
+int32_t h3a_attention_noalloc(const void* q, const void* k_store, const void* v_store, const void* scales,
+                              int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, float softmax_scale,
+                              int64_t q_chunk, int64_t kv_block, int32_t mode, const uint8_t* tile_mask, void* out,
+                              void* stream) {
+  return attention_call(q, k_store, v_store, scales, s_q, s_kv, n_heads, head_dim, softmax_scale, q_chunk, kv_block,
+                        mode, tile_mask, out, nullptr, 0, true, stream);
 }
 
 int32_t h3a_attention_routed(const void* q, const void* k_bf16, const void* v_bf16, const void* k_codes,

@@ -189,3 +189,32 @@ def test_workspace_sizes(lib):
     n_kt = 16
     assert sol >= hard + 2 * (2 * n_kt * 128 * 2) + 2 * n_kt * 4 + 2 * 4 * n_kt * 4
     assert h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, "exact", False, sol=True) == 0
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define H3A_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == h3a.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("q_chunk,heads,mode,mask", [(65536, 32, 1, None), (16384, 32, 1, None),
+                                                     (8192, 64, 2, None), (16384, 32, 0x101, 1)])
+def test_noalloc_rejects_requests_above_its_scratch(lib, q_chunk, heads, mode, mask):
+    # Checked from the sizes alone, before any pointer or GPU call: nothing is queued.
+    need = h3a.h3a_attention_workspace_bytes(65536, 65536, heads, q_chunk, mode, mask is not None)
+    assert need > h3a.NOALLOC_SCRATCH_BYTES
+    rc = lib.h3a_attention_noalloc(None, None, None, 16 if mode else None, 65536, 65536, heads, 128, 0.088, q_chunk,
+                                   0, mode, mask, None, None)
+    assert rc == -4
+    err = lib.h3a_last_error().decode()
+    assert "h3a_attention_noalloc" in err and str(need) in err
+
+
+def test_noalloc_checks_arguments_like_h3a_attention(lib):
+    assert lib.h3a_attention_noalloc(None, None, None, 16, 1024, 1024, 2, 64, 0.088, 256, 0, 1, None, None,
+                                     None) == -2
+    assert lib.h3a_attention_noalloc(None, None, None, None, 1024, 1024, 2, 128, 0.088, 256, 0, 1, None, None,
+                                     None) == -1
+    assert "scales" in lib.h3a_last_error().decode()
+    assert lib.h3a_attention_noalloc(None, None, None, 16, 0, 1024, 2, 128, 0.088, 256, 0, 1, None, None,
+                                     None) == 0
