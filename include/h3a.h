@@ -66,6 +66,16 @@ extern "C" {
  * block-sum V [P3 Nodes, routed geometry]). */
 #define H3A_SOL 0x100
 
+/* Flag OR-ed into H3A_MODE_KVI8R or H3A_MODE_KVI8R32: `out` is fp16 instead of
+ * bf16.  kvi8r attention runs in fp16 [P1 kv_store; P2 "The K/V store options":
+ * why fp16 and not bf16 inside kvi8r], and fp16 keeps that precision in the
+ * output: rounding the exact result to fp16 costs about 2e-4 relative (RMS)
+ * against about 1.7e-3 for bf16, whose half-ulp above 2.0 alone is 7.8e-3.
+ * The row is un-rotated in fp32 and rounded once, to fp16 here or to bf16
+ * without the flag, so the two outputs are two roundings of one value.  With
+ * the exact store it is H3A_EINVAL (that output is bf16). */
+#define H3A_OUT_F16 0x200
+
 /* ABI version of the loaded library; callers compare it with H3A_ABI_VERSION. */
 int32_t h3a_abi_version(void);
 
@@ -136,7 +146,7 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
  *   O[t, h, :] = sum_j softmax_j(softmax_scale * q[t,h,:] . k[j,h,:]) v[j,h,:]
  *
  * mode is H3A_MODE_EXACT_BF16, H3A_MODE_KVI8R or H3A_MODE_KVI8R32, optionally OR-ed
- * with H3A_SOL.
+ * with H3A_SOL and (kvi8r stores) H3A_OUT_F16.
  * mode H3A_MODE_EXACT_BF16: k_store / v_store are bf16 [s_kv, n_heads, 128]
  *   (token-major), scales must be NULL.  Inputs feed bf16 matrix cores, fp32
  *   accumulation.  The output is bitwise identical for every q_chunk and
@@ -153,7 +163,8 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
  *   rounded to fp16) before the fp16 matrix-core products.
  *
  * q:          bf16 [s_q, n_heads, 128], 16-byte aligned.
- * out:        bf16 [s_q, n_heads, 128], 16-byte aligned; must not alias inputs.
+ * out:        bf16 [s_q, n_heads, 128] (fp16 with H3A_OUT_F16), 16-byte
+ *             aligned; must not alias inputs.
  * q_chunk:    query tokens per pass (>= 1; a multiple of 64 when tile_mask is
  *             given).  Query chunks are attended one after another on `stream`.
  * kv_block:   K/V block length of the online-softmax (log-sum-exp) combine:
@@ -223,6 +234,8 @@ int32_t h3a_attention_noalloc(const void* q, const void* k_store, const void* v_
  * h3a_attention gives it in that mode.  Rows are attended in increasing
  * order, each stretch of one mode in passes of at most q_chunk rows.
  *
+ * out:         bf16 [s_q, n_heads, 128] for every row (no H3A_OUT_F16 here:
+ *              both stores' rows go to one bf16 tensor).
  * exact_spans: HOST memory, n_spans pairs of int64 (begin, end) with
  *              0 <= begin <= end <= s_q, increasing and disjoint
  *              (end_i <= begin_{i+1}); NULL when n_spans == 0.  Read during
@@ -263,6 +276,8 @@ size_t h3a_attention_host_kv_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t 
  *              PINNED host memory (hipHostMalloc), 16-byte aligned; pageable
  *              memory is H3A_EINVAL.  Must stay valid and unchanged until the
  *              work queued on `stream` has finished.
+ * mode:        a store kind as for h3a_attention, optionally OR-ed with
+ *              H3A_OUT_F16 (kvi8r stores; no H3A_SOL: dense only).
  * q, out:      device memory, as for h3a_attention.
  * workspace:   h3a_attention_host_kv_workspace_bytes(...) bytes of device
  *              memory (two K/V blocks, one query chunk's state).

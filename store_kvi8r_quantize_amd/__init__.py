@@ -29,6 +29,7 @@ MODE_KVI8R = 1
 MODE_KVI8R32 = 2  # kvi8r with one fp16 scale per 32 rotated values
 MODES = {"exact": MODE_EXACT_BF16, "bf16": MODE_EXACT_BF16, "kvi8r": MODE_KVI8R, "kvi8r32": MODE_KVI8R32}
 SOL = 0x100  # H3A_SOL: dropped tiles of a tile_mask enter as one pseudo-key each
+OUT_F16 = 0x200  # H3A_OUT_F16: fp16 output rows for the kvi8r stores (chosen here from out's dtype)
 NOALLOC_SCRATCH_BYTES = 256 << 20  # H3A_NOALLOC_SCRATCH_BYTES: the library's own scratch per GPU
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libh3a.so")
@@ -130,6 +131,19 @@ def _workspace(need: int, device, stream_obj):
         return torch.empty(need, dtype=torch.uint8, device=device)
 
 
+def _out_flag(out, mode) -> int:
+    """H3A_OUT_F16 when out is fp16 (kvi8r stores only), 0 when it is bf16."""
+    if not isinstance(out, torch.Tensor) or not out.is_cuda:
+        raise TypeError("out must be a GPU tensor")
+    if out.dtype == torch.float16:
+        if mode not in (MODE_KVI8R, MODE_KVI8R32):
+            raise TypeError("an fp16 out is for the kvi8r stores; the exact store's output is bf16")
+        return OUT_F16
+    if out.dtype != torch.bfloat16:
+        raise TypeError(f"out must be bfloat16 (or float16 for the kvi8r stores), got {out.dtype}")
+    return 0
+
+
 def _need(t, name, dtype):
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a GPU tensor")
@@ -194,9 +208,8 @@ def h3a_attention(q, k_store, v_store, scales, out, *, q_chunk: int, kv_block: i
     """
     lib = _load()
     mode = MODES.get(mode, mode)
-    flags = SOL if sol else 0
+    flags = (SOL if sol else 0) | _out_flag(out, mode)
     _need(q, "q", torch.bfloat16)
-    _need(out, "out", torch.bfloat16)
     if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be contiguous [s_q, n_heads, head_dim] tensors of equal shape")
     s_q, n_heads, head_dim = q.shape
@@ -240,9 +253,8 @@ def h3a_attention_noalloc(q, k_store, v_store, scales, out, *, q_chunk: int, kv_
     scratch, so calls on different streams must not overlap."""
     lib = _load()
     mode = MODES.get(mode, mode)
-    flags = SOL if sol else 0
+    flags = (SOL if sol else 0) | _out_flag(out, mode)
     _need(q, "q", torch.bfloat16)
-    _need(out, "out", torch.bfloat16)
     if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be contiguous [s_q, n_heads, head_dim] tensors of equal shape")
     s_q, n_heads, head_dim = q.shape
@@ -322,8 +334,8 @@ def h3a_attention_host_kv(q, k_host, v_host, scales_host, out, *, q_chunk: int, 
     one kv_block at a time.  Store layouts as for h3a_attention; q and out are GPU tensors."""
     lib = _load()
     mode = MODES.get(mode, mode)
+    flags = _out_flag(out, mode)
     _need(q, "q", torch.bfloat16)
-    _need(out, "out", torch.bfloat16)
     if not (q.is_contiguous() and out.is_contiguous()) or q.dim() != 3 or out.shape != q.shape:
         raise ValueError("q and out must be contiguous [s_q, n_heads, head_dim] tensors of equal shape")
     want = torch.bfloat16 if mode == MODE_EXACT_BF16 else torch.int8
@@ -346,8 +358,8 @@ def h3a_attention_host_kv(q, k_host, v_host, scales_host, out, *, q_chunk: int, 
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     hp = lambda t: None if t is None else t.data_ptr()
     _check(lib.h3a_attention_host_kv(_ptr(q), hp(k_host), hp(v_host), hp(scales_host), s_q, s_kv, n_heads, head_dim,
-                                     float(softmax_scale), int(q_chunk), int(kv_block), int(mode), _ptr(out),
-                                     _ptr(workspace), ws_bytes, st.cuda_stream))
+                                     float(softmax_scale), int(q_chunk), int(kv_block), int(mode) | flags,
+                                     _ptr(out), _ptr(workspace), ws_bytes, st.cuda_stream))
     return out
 
 

@@ -298,6 +298,7 @@ hipError_t copy_stream(hipStream_t* out) {
 struct Pass {
   int32_t mode = 0;
   bool sol = false;
+  bool out_f16 = false;  // kvi8r modes: fp16 output rows (H3A_OUT_F16), else bf16
   const uint16_t* q = nullptr;
   uint16_t* out = nullptr;
   const void* k = nullptr;
@@ -394,7 +395,7 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
     if (p.timing && (e = timer.end(p.st)) != hipSuccess) return hip_fail(e, "timing event");
     if (p.mode != H3A_MODE_EXACT_BF16) {
       if ((e = h3a::launch_unrotate_o(reinterpret_cast<const float*>(p.ws + p.wl.orot), p.out + off,
-                                      rows * p.n_heads, p.st)) != hipSuccess)
+                                      rows * p.n_heads, p.out_f16, p.st)) != hipSuccess)
         return hip_fail(e, "unrotate_o launch");
     }
   }
@@ -465,11 +466,13 @@ int attention_call(const void* q, const void* k_store, const void* v_store, cons
                    size_t workspace_bytes, bool use_scratch, void* stream) {
   g_err.clear();
   if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
-  const bool sol = (mode & H3A_SOL) != 0;
+  const bool sol = (mode & H3A_SOL) != 0, out_f16 = (mode & H3A_OUT_F16) != 0;
   const int32_t mode_arg = mode;
-  mode &= ~H3A_SOL;
+  mode &= ~(H3A_SOL | H3A_OUT_F16);
   if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32)
     return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
+  if (out_f16 && mode == H3A_MODE_EXACT_BF16)
+    return fail(H3A_EINVAL, "H3A_OUT_F16 applies to the kvi8r stores; the exact store's output is bf16");
   if (sol && tile_mask == nullptr) return fail(H3A_EINVAL, "H3A_SOL needs a tile_mask");
   if (sol && s_kv > h3a::kSolMaxKv) return fail(H3A_EINVAL, "H3A_SOL supports s_kv up to 2^30 - 64");
   int rc;
@@ -509,6 +512,7 @@ int attention_call(const void* q, const void* k_store, const void* v_store, cons
                      stream);
   p.tile_mask = tile_mask;
   p.sol = sol;
+  p.out_f16 = out_f16;
   if (sol) {
     hipError_t e = h3a::launch_tile_means(mode, k_store, v_store, p.k_scale, p.v_scale, s_kv, n_heads,
                                           reinterpret_cast<uint16_t*>(p.ws + wl.kmean),
@@ -543,7 +547,7 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
                                      int32_t mode, int32_t sparse) {
   if (head_dim != H3A_HEAD_DIM || n_heads < 1 || s_kv < 0) return 0;
   const bool sol = (mode & H3A_SOL) != 0;
-  mode &= ~H3A_SOL;
+  mode &= ~(H3A_SOL | H3A_OUT_F16);
   if ((mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32) || (sol && !sparse))
     return 0;
   WorkspaceLayout w;
@@ -617,6 +621,7 @@ int32_t h3a_attention_routed(const void* q, const void* k_bf16, const void* v_bf
 size_t h3a_attention_host_kv_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim,
                                              int64_t q_chunk, int64_t kv_block, int32_t mode) {
   if (head_dim != H3A_HEAD_DIM || n_heads < 1 || s_kv < 0 || kv_block < 0 || kv_block % H3A_TILE != 0) return 0;
+  mode &= ~H3A_OUT_F16;
   if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32) return 0;
   StagedLayout w;
   if (!staged_layout(s_q, s_kv, n_heads, q_chunk, kv_block, mode, &w)) return 0;
@@ -629,8 +634,13 @@ int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_h
                               size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  const bool out_f16 = (mode & H3A_OUT_F16) != 0;
+  const int32_t mode_arg = mode;
+  mode &= ~H3A_OUT_F16;
   if (mode != H3A_MODE_EXACT_BF16 && mode != H3A_MODE_KVI8R && mode != H3A_MODE_KVI8R32)
-    return fail(H3A_EINVAL, "unknown mode %d", mode);
+    return fail(H3A_EINVAL, "unknown mode %d", mode_arg);
+  if (out_f16 && mode == H3A_MODE_EXACT_BF16)
+    return fail(H3A_EINVAL, "H3A_OUT_F16 applies to the kvi8r stores; the exact store's output is bf16");
   int rc;
   if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
   if (mode != H3A_MODE_EXACT_BF16 && scales_host == nullptr && s_kv > 0)
@@ -659,6 +669,7 @@ int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_h
   char* ws = static_cast<char*>(workspace);
   Pass p = make_pass(mode, q, out, nullptr, nullptr, nullptr, s_q, s_kv, n_heads, softmax_scale, q_chunk, ws,
                      wl.base, stream);
+  p.out_f16 = out_f16;
   if (s_kv == 0) return attend_rows(p, 0, s_q);  // no K/V: every row is zero
 
   hipStream_t cs;
@@ -744,7 +755,7 @@ int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_h
     }
     if (status == H3A_OK && mode != H3A_MODE_EXACT_BF16)
       check(h3a::launch_unrotate_o(reinterpret_cast<const float*>(ws + wl.base.orot), p.out + off, rows * n_heads,
-                                   p.st),
+                                   p.out_f16, p.st),
             "unrotate_o launch");
   }
   destroy();
@@ -770,7 +781,8 @@ int32_t h3a_unrotate_rows(const float* x_f32, void* y_bf16, int64_t n_rows, void
   int rc;
   if ((rc = check_buffer(x_f32, (uint64_t)n_rows * 512, 16, "x")) != H3A_OK) return rc;
   if ((rc = check_buffer(y_bf16, (uint64_t)n_rows * 256, 16, "y")) != H3A_OK) return rc;
-  hipError_t e = h3a::launch_unrotate_o(x_f32, static_cast<uint16_t*>(y_bf16), n_rows, static_cast<hipStream_t>(stream));
+  hipError_t e =
+      h3a::launch_unrotate_o(x_f32, static_cast<uint16_t*>(y_bf16), n_rows, false, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3A_OK : hip_fail(e, "unrotate_o launch");
 }
 

@@ -14,7 +14,8 @@ hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int6
                                  uint16_t* scales, bool grouped, hipStream_t stream);
 
 hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
-hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
+// f16: write fp16 rows, else bf16.
+hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, bool f16, hipStream_t stream);
 
 // One query chunk of attention.
 struct AttnChunk {

@@ -6,7 +6,7 @@
 //
 // Same lane layout as kvi8r_quantize: 4 lanes per 128-value row, 16 rows per
 // wave.  Both kernels are HBM-bound streams: rotate reads 256 B and writes 256 B
-// per row; unrotate reads 512 B and writes 256 B per row.
+// per row; unrotate reads 512 B and writes 256 B per row (fp16 or bf16).
 #include "h3a_device.h"
 #include "launch.h"
 
@@ -44,6 +44,8 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(const uint16_t* __restric
   }
 }
 
+// F16: the output is fp16 (the precision kvi8r attention runs in), else bf16.
+template <bool F16>
 __global__ __launch_bounds__(256) void unrotate_o_kernel(const float* __restrict__ x,
                                                          uint16_t* __restrict__ y, int64_t n_rows) {
   const int lane = threadIdx.x & 63;
@@ -69,8 +71,10 @@ __global__ __launch_bounds__(256) void unrotate_o_kernel(const float* __restrict
   for (int k = 0; k < 4; ++k) {
     u32x4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = pack_bf16x2(v[8 * k + 2 * i] * kInvSqrt128f, v[8 * k + 2 * i + 1] * kInvSqrt128f);
+    for (int i = 0; i < 4; ++i) {
+      const float a = v[8 * k + 2 * i] * kInvSqrt128f, b = v[8 * k + 2 * i + 1] * kInvSqrt128f;
+      w[i] = F16 ? pack_f16x2(a, b) : pack_bf16x2(a, b);
+    }
     *reinterpret_cast<u32x4*>(dst + 32 * k + 8 * sub) = w;
   }
 }
@@ -84,10 +88,13 @@ hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, hipSt
   return hipGetLastError();
 }
 
-hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, hipStream_t stream) {
+hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, bool f16, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(unrotate_o_kernel, dim3((unsigned)((n_rows + 63) / 64)), dim3(256), 0, stream, x, y,
-                     n_rows);
+  const dim3 grid((unsigned)((n_rows + 63) / 64));
+  if (f16)
+    hipLaunchKernelGGL(unrotate_o_kernel<true>, grid, dim3(256), 0, stream, x, y, n_rows);
+  else
+    hipLaunchKernelGGL(unrotate_o_kernel<false>, grid, dim3(256), 0, stream, x, y, n_rows);
   return hipGetLastError();
 }
 

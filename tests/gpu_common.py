@@ -28,6 +28,19 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+def out_like(q: torch.Tensor, mode: str) -> torch.Tensor:
+    """Output of an attention call: fp16 for the kvi8r stores (the precision kvi8r attention runs in, and the
+    output the tolerances are stated for), bf16 for the exact store."""
+    return torch.empty(q.shape, dtype=torch.float16 if mode in ("kvi8r", "kvi8r32") else torch.bfloat16,
+                       device=q.device)
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact fp64 values of an fp16 or bf16 output tensor."""
+    bits = host_u16(t)
+    return oracle.f16_to_f64(bits) if t.dtype == torch.float16 else oracle.bf16_to_f64(bits)
+
+
 def gpu_inputs(w: synth.Workload, tensors=("q", "k", "v")) -> dict:
     """Token-major bf16 GPU tensors [S, H, 128], drawn head by head straight to the device."""
     import threading
@@ -109,7 +122,7 @@ def pool_check(pool, kind, w, out, heads, rows_of, store=None, mask=None, tag=""
     for h in heads:
         rows = np.asarray(rows_of(h))
         spec = {"kind": kind, "workload": w, "head": h, "rows": rows, "s_kv": s_kv,
-                "got": host_u16(out[torch.from_numpy(rows).cuda(), h])}
+                "got": host_u16(out[torch.from_numpy(rows).cuda(), h]), "got_f16": out.dtype == torch.float16}
         if store is not None:
             spec["store"] = store_head(*store, h)
         if mask is not None:
@@ -120,6 +133,8 @@ def pool_check(pool, kind, w, out, heads, rows_of, store=None, mask=None, tag=""
         say(tag, kind, "head", r["head"], "rows", r["rows"], "relL2", r["rel_l2"], "max abs", r["max_abs"])
         results.append(r)
     gate = {"sol_exact": "exact", "sol_kvi8r": "kvi8r"}.get(kind, kind)
+    if gate == "kvi8r" and out.dtype == torch.bfloat16:
+        gate = "kvi8r_bf16"
     summary = assert_attention_ok(results, gate)
     say(tag, kind, "summary", summary)
     return summary

@@ -115,15 +115,24 @@ def reference_rows(kind: str, w: synth.Workload, h: int, rows: np.ndarray, store
     return oracle.kvi8r_attention(qf, kc, ks, vc, vs, SCALE, keep)
 
 
+def half_ulp(x: np.ndarray, mantissa_bits: int) -> np.ndarray:
+    """Half an ulp of |x| in a binary format with that many stored mantissa bits (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -14)))
+    return 2.0 ** (e - mantissa_bits - 1)
+
+
 def attention_job(spec: dict) -> dict:
-    """One head: oracle rows against the GPU's rows (bf16 bits), error statistics only."""
+    """One head: oracle rows against the GPU's rows (fp16 bits if spec["got_f16"], else bf16), error
+    statistics only.  "max_abs_beyond_bf16" is the largest error left after allowing each element the
+    two roundings that separate a bf16 output from the fp16 one (half an ulp of each format)."""
     ref = reference_rows(spec["kind"], spec["workload"], spec["head"], spec["rows"], spec.get("store"),
                          spec.get("mask"), spec.get("s_kv"))
-    got = oracle.bf16_to_f64(spec["got"])
+    got = (oracle.f16_to_f64 if spec.get("got_f16") else oracle.bf16_to_f64)(spec["got"])
     d = got - ref
+    beyond = np.abs(d) - half_ulp(ref, 7) - half_ulp(ref, 10)
     return {"head": spec["head"], "rows": len(spec["rows"]), "rel_l2": rel_l2(got, ref),
             "max_abs": float(np.abs(d).max()) if d.size else 0.0, "err2": float(np.sum(d * d)),
-            "ref2": float(np.sum(ref * ref))}
+            "ref2": float(np.sum(ref * ref)), "max_abs_beyond_bf16": float(beyond.max()) if d.size else 0.0}
 
 
 def quantize_job(spec: dict) -> dict:
@@ -147,9 +156,13 @@ def summarise(results: list, mode: str) -> dict:
 
 
 def assert_attention_ok(results: list, mode: str) -> dict:
-    """The gates, per head and pooled."""
+    """The gates, per head and pooled.  mode "kvi8r_bf16": a kvi8r store's output delivered in bf16, whose
+    elements may differ from the gated fp16 output by the two roundings (see attention_job)."""
     s = summarise(results, mode)
-    if mode in ("kvi8r", "kvi8r32", "sol_kvi8r"):
+    if mode == "kvi8r_bf16":
+        bad = [r for r in results if not (r["rel_l2"] <= KVI8R_REL_L2 and r["max_abs_beyond_bf16"] <= KVI8R_MAX_ABS)]
+        assert not bad and s["rel_l2"] <= KVI8R_REL_L2, (s, bad)
+    elif mode in ("kvi8r", "kvi8r32", "sol_kvi8r"):
         bad = [r for r in results if not (r["rel_l2"] <= KVI8R_REL_L2 and r["max_abs"] <= KVI8R_MAX_ABS)]
         assert not bad and s["rel_l2"] <= KVI8R_REL_L2 and s["max_abs"] <= KVI8R_MAX_ABS, (s, bad)
     else:

@@ -71,7 +71,9 @@ def _attn(lib, **kw):
     (dict(mode=0, scales=16), -1, "no scales"),
     (dict(mode=0x100 | 1, scales=16), -1, "H3A_SOL needs a tile_mask"),
     (dict(mode=0x100 | 7, mask=1), -1, "mode"),
-    (dict(mode=0x200 | 1, mask=1, scales=16), -1, "mode"),
+    (dict(mode=0x400 | 1, mask=1, scales=16), -1, "mode"),
+    (dict(mode=0x200 | 0), -1, "H3A_OUT_F16"),
+    (dict(mode=0x200 | 0x100 | 0, mask=1), -1, "H3A_OUT_F16"),
     (dict(mode=0x100 | 1, mask=1, scales=16, s_kv=(1 << 30) - 63), -1, "2^30 - 64"),
 ])
 def test_attention_rejects_bad_arguments(lib, kw, status, msg):
@@ -147,6 +149,8 @@ def test_quantize_g32_rejects_bad_arguments(lib):
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(head_dim=64), -2, "head_dim"),
     (dict(mode=3), -1, "mode"),
+    (dict(mode=0x200 | 0, scales=None), -1, "H3A_OUT_F16"),
+    (dict(mode=0x100 | 1), -1, "mode"),
     (dict(mode=1, scales=None), -1, "scales"),
     (dict(mode=0, scales=16), -1, "no scales"),
     (dict(kv_block=100), -1, "kv_block"),
@@ -218,3 +222,12 @@ def test_noalloc_checks_arguments_like_h3a_attention(lib):
     assert "scales" in lib.h3a_last_error().decode()
     assert lib.h3a_attention_noalloc(None, None, None, 16, 0, 1024, 2, 128, 0.088, 256, 0, 1, None, None,
                                      None) == 0
+
+
+def test_out_f16_flag_does_not_change_workspace_sizes():
+    for mode in (1, 2):
+        for sparse in (False, True):
+            assert h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, mode | 0x200, sparse) == \
+                h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, mode, sparse) > 0
+    assert h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 256, 1 | 0x200) == \
+        h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 256, 1)

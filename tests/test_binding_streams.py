@@ -80,6 +80,7 @@ def rig(monkeypatch):
     monkeypatch.setattr(h3a, "_load", lambda: lib)
     monkeypatch.setattr(h3a, "_lib", lib)
     monkeypatch.setattr(h3a, "_need", lambda *a: None)
+    monkeypatch.setattr(h3a, "_out_flag", lambda out, mode: 0)
     monkeypatch.setattr(h3a, "_stream_obj", lambda t, s: side)
     return rec, lib, side
 

@@ -16,7 +16,8 @@ import oracle
 import store_kvi8r_quantize_amd as h3a
 import synth
 from gpu_common import (EXACT_REL_L2, KVI8R_MAX_ABS, KVI8R_REL_L2, HeadSource, build_store, gpu_inputs, gpu_u16,
-                        host_u16, oracle_exact_rows, oracle_kvi8r_rows, pool_check, rel_l2, say, store_head)
+                        host_u16, oracle_exact_rows, oracle_kvi8r_rows, out_f64, out_like, pool_check, rel_l2, say,
+                        store_head)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +39,8 @@ def _inputs(name):
     return _CACHE[name]
 
 
-def _run(mode, q, k, v, store=None, q_chunk=256, kv_block=0, mask=None):
-    out = torch.empty_like(q)
+def _run(mode, q, k, v, store=None, q_chunk=256, kv_block=0, mask=None, out_dtype=None):
+    out = out_like(q, mode) if out_dtype is None else torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if mode == "kvi8r":
         kc, vc, sc = store
         h3a.h3a_attention(q, kc, vc, sc, out, q_chunk=q_chunk, kv_block=kv_block, mode="kvi8r", tile_mask=mask)
@@ -59,7 +60,7 @@ def _check(mode, heads, src, out, store, rows_of, mask=None, tag=""):
             ref = oracle_kvi8r_rows(src, store_head(*store, h), h, rows, mask)
         else:
             ref = oracle_exact_rows(src, h, rows, mask)
-        got = oracle.bf16_to_f64(host_u16(out[torch.from_numpy(rows).cuda(), h]))
+        got = out_f64(out[torch.from_numpy(rows).cuda(), h])
         r = rel_l2(got, ref)
         worst = max(worst, r)
         mx = max(mx, float(np.abs(got - ref).max()))
@@ -135,7 +136,7 @@ def test_zero_query_averages_values(mode):
     q = torch.zeros_like(g["q"])
     store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
     out = _run(mode, q, g["k"], g["v"], store)
-    got = oracle.bf16_to_f64(host_u16(out))
+    got = out_f64(out)
     for h in range(w.heads):
         if mode == "kvi8r":
             kc, ks, vc, vs = store_head(*store, h)
@@ -156,6 +157,26 @@ def test_q_chunk_and_kv_block_bitwise_invariance(mode):
         say("outlier64k", mode, "q_chunk", q_chunk, "kv_block", kv_block, "bitwise equal", same)
         assert same
 
+
+
+@pytest.mark.timeout(600)
+def test_kvi8r_bf16_output(oracle_pool):
+    # The kvi8r store's output delivered in bf16 (the model dtype) is the same fp32 value rounded to bf16
+    # instead of fp16: elementwise the two differ by at most half an ulp of each format, and against the
+    # oracle the bf16 output keeps relative L2 <= 2e-3 (every row of outlier16k).
+    w, bits, g = _inputs("outlier16k")
+    store = build_store(g["k"], g["v"], kv_chunk=w.q_chunk)
+    f16 = _run("kvi8r", g["q"], g["k"], g["v"], store, q_chunk=w.q_chunk)
+    b16 = _run("kvi8r", g["q"], g["k"], g["v"], store, q_chunk=w.q_chunk, out_dtype=torch.bfloat16)
+    f, b = out_f64(f16), out_f64(b16)
+    from parity import half_ulp
+
+    top = np.maximum(np.abs(f), np.abs(b))
+    excess = np.abs(b - f) - half_ulp(top, 7) - half_ulp(top, 10)
+    say("kvi8r bf16 vs fp16 output: max |b - f|", float(np.abs(b - f).max()), "max excess", float(excess.max()))
+    assert np.all(excess <= 0)
+    pool_check(oracle_pool, "kvi8r", w, b16, range(w.heads), lambda h: np.arange(w.seq), store,
+               tag="outlier16k-bf16-out")
 
 
 @pytest.mark.timeout(900)
@@ -229,7 +250,7 @@ def test_side_stream_with_binding_workspace(raw_handle):
     need = h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, 4096, "kvi8r", False)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
-    out = torch.empty_like(g["q"])
+    out = out_like(g["q"], "kvi8r")
     for _ in range(3):
         h3a.h3a_attention(g["q"], *store, out, q_chunk=4096, mode="kvi8r",
                           stream=side.cuda_stream if raw_handle else side)

@@ -16,8 +16,8 @@ import torch
 import oracle
 import store_kvi8r_quantize_amd as h3a
 import synth
-from gpu_common import (KVI8R_MAX_ABS, KVI8R_REL_L2, SCALE, build_store, gpu_inputs, gpu_u16, host_u16, rel_l2,
-                        say, store_head)
+from gpu_common import (KVI8R_MAX_ABS, KVI8R_REL_L2, SCALE, build_store, gpu_inputs, gpu_u16, host_u16, out_f64,
+                        out_like, rel_l2, say, store_head)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +40,7 @@ def _store(mode, k, v, kv_chunk=None):
 
 
 def _device(mode, q, store, q_chunk):
-    out = torch.empty_like(q)
+    out = out_like(q, mode)
     h3a.h3a_attention(q, *store, out, q_chunk=q_chunk, mode=mode)
     return out
 
@@ -48,7 +48,7 @@ def _device(mode, q, store, q_chunk):
 def _staged(mode, q, store, q_chunk, kv_block):
     host = [None if t is None else _pinned(t) for t in store]
     torch.cuda.synchronize()
-    out = torch.empty_like(q)
+    out = out_like(q, mode)
     h3a.h3a_attention_host_kv(q, *host, out, q_chunk=q_chunk, kv_block=kv_block, mode=mode)
     torch.cuda.synchronize()
     return out
@@ -83,7 +83,7 @@ def test_staged_kvi8r_against_oracle():
     for h in range(w.heads):
         kc, ks, vc, vs = store_head(*store, h)
         ref_all.append(oracle.kvi8r_attention(oracle.bf16_to_f64(bits["q"][:, h]), kc, ks, vc, vs, SCALE))
-        got_all.append(oracle.bf16_to_f64(host_u16(out[:, h])))
+        got_all.append(out_f64(out[:, h]))
     got, ref = np.concatenate(got_all), np.concatenate(ref_all)
     r, mx = rel_l2(got, ref), float(np.abs(got - ref).max())
     say("staged tiny kvi8r relL2", r, "max abs", mx)

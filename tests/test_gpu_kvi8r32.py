@@ -18,7 +18,7 @@ import oracle
 import store_kvi8r_quantize_amd as h3a
 import synth
 from gpu_common import (KVI8R_MAX_ABS, KVI8R_REL_L2, SCALE, assert_quantize_ok, gpu_inputs, gpu_u16, host_u16,
-                        quantize_report, rel_l2, say)
+                        out_f64, out_like, quantize_report, rel_l2, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -85,7 +85,7 @@ def test_chunked_build_equals_one_shot():
 
 
 def _attend(q, store, q_chunk, mask=None, sol=False):
-    out = torch.empty_like(q)
+    out = out_like(q, "kvi8r32")
     h3a.h3a_attention(q, *store, out, q_chunk=q_chunk, mode="kvi8r32", tile_mask=mask, sol=sol)
     torch.cuda.synchronize()
     return out
@@ -98,7 +98,7 @@ def _check_rows(bits_q, store, out, heads, rows_of, tag, ref_fn=None):
         kc, ks, vc, vs = _head(store, h)
         q = oracle.bf16_to_f64(bits_q(h)[rows])
         ref = ref_fn(h, rows, q, kc, ks, vc, vs) if ref_fn else oracle.kvi8r_attention(q, kc, ks, vc, vs, SCALE)
-        got_all.append(oracle.bf16_to_f64(host_u16(out[torch.from_numpy(rows).cuda(), h])))
+        got_all.append(out_f64(out[torch.from_numpy(rows).cuda(), h]))
         ref_all.append(ref)
     got, ref = np.concatenate(got_all), np.concatenate(ref_all)
     r, mx = rel_l2(got, ref), float(np.abs(got - ref).max())
@@ -159,7 +159,7 @@ def test_finer_scales_land_closer_to_unquantised_attention():
     kc, vc, sc = h3a.new_kvi8r_store(w.seq, w.heads)
     h3a.h3a_kv_quantize(g["k"], kc, sc[0])
     h3a.h3a_kv_quantize(g["v"], vc, sc[1])
-    out8 = torch.empty_like(g["q"])
+    out8 = out_like(g["q"], "kvi8r")
     h3a.h3a_attention(g["q"], kc, vc, sc, out8, q_chunk=4096, mode="kvi8r")
     torch.cuda.synchronize()
     g32, g8, ref_all = [], [], []
@@ -168,8 +168,8 @@ def test_finer_scales_land_closer_to_unquantised_attention():
         ref_all.append(oracle.exact_attention_bf16(bits_q(h)[rows], synth.head_bf16(w, "k", h),
                                                    synth.head_bf16(w, "v", h), SCALE))
         idx = torch.from_numpy(rows).cuda()
-        g32.append(oracle.bf16_to_f64(host_u16(out32[idx, h])))
-        g8.append(oracle.bf16_to_f64(host_u16(out8[idx, h])))
+        g32.append(out_f64(out32[idx, h]))
+        g8.append(out_f64(out8[idx, h]))
     ref = np.concatenate(ref_all)
     e32, e8 = rel_l2(np.concatenate(g32), ref), rel_l2(np.concatenate(g8), ref)
     say("against unquantised attention: kvi8r32", e32, "kvi8r", e8)

@@ -78,8 +78,12 @@ def test_routed_against_oracle():
     got, ref = np.stack(got_all, 1), np.stack(ref_all, 1)
     re = rel_l2(got[rows], ref[rows])
     rq = rel_l2(got[~rows], ref[~rows])
-    mq = float(np.abs(got[~rows] - ref[~rows]).max())
-    say("routed tiny: exact rows relL2", re, "kvi8r rows relL2", rq, "max abs", mq)
+    # routed output is bf16 for every row: kvi8r rows get the two half-ulps that separate it from fp16
+    from parity import half_ulp
+
+    dq = np.abs(got[~rows] - ref[~rows]) - half_ulp(ref[~rows], 7) - half_ulp(ref[~rows], 10)
+    mq = float(dq.max())
+    say("routed tiny: exact rows relL2", re, "kvi8r rows relL2", rq, "max abs beyond the bf16 rounding", mq)
     assert re <= EXACT_REL_L2
     assert rq <= KVI8R_REL_L2 and mq <= KVI8R_MAX_ABS
 

@@ -20,14 +20,14 @@ import torch
 import oracle
 import store_kvi8r_quantize_amd as h3a
 import synth
-from gpu_common import (EXACT_REL_L2, KVI8R_MAX_ABS, KVI8R_REL_L2, SCALE, build_store, gpu_u16, host_u16, rel_l2,
-                        say, store_head)
+from gpu_common import (EXACT_REL_L2, KVI8R_MAX_ABS, KVI8R_REL_L2, SCALE, build_store, gpu_u16, host_u16, out_f64,
+                        out_like, rel_l2, say, store_head)
 
 pytestmark = pytest.mark.gpu
 
 
 def _run(mode, q, k, v, store, q_chunk, mask, sol=True):
-    out = torch.empty_like(q)
+    out = out_like(q, mode)
     if mode == "kvi8r":
         kc, vc, sc = store
         h3a.h3a_attention(q, kc, vc, sc, out, q_chunk=q_chunk, mode="kvi8r", tile_mask=mask, sol=sol)
@@ -58,7 +58,7 @@ def _assert_close(mode, got, ref, tag):
 
 
 def _rows_out(out, rows, h):
-    return oracle.bf16_to_f64(host_u16(out[torch.from_numpy(np.asarray(rows)).cuda(), h]))
+    return out_f64(out[torch.from_numpy(np.asarray(rows)).cuda(), h])
 
 
 @pytest.mark.parametrize("mode", ["exact", "kvi8r"])
@@ -129,7 +129,7 @@ def test_sol_all_kept_equals_dense_bitwise(mode):
     store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
     nt = w.n_tiles
     ones = torch.ones((w.heads, nt, nt), dtype=torch.uint8, device="cuda")
-    dense = torch.empty_like(g["q"])
+    dense = out_like(g["q"], mode)
     if mode == "kvi8r":
         h3a.h3a_attention(g["q"], *store, dense, q_chunk=4096, mode="kvi8r")
     else:
