@@ -56,6 +56,7 @@
 
 #include "h3a_device.h"
 #include "launch.h"
+#include "tile_span.h"
 
 namespace h3a {
 
@@ -129,9 +130,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // the bytes from memory at 217088 tokens, by the FETCH_SIZE counter.)  A
 // negative kt is read as tile 0, so no buffer base can precede the store.
 __device__ __forceinline__ uint32_t store_span(const AttnChunk& a, int kt, uint32_t row_bytes, uint32_t last_bytes) {
-  const int32_t rows = (int32_t)a.s_kv - (kt > 0 ? kt : 0) * kTile;
+  const int32_t rows = rows_to_end(a.s_kv, kt);
   if (rows <= 0) return 0u;  // an empty store: every load reads 0
-  const uint64_t b = (uint64_t)(uint32_t)(rows - 1) * row_bytes + last_bytes;
+  const uint64_t b = span_bytes(rows, row_bytes, last_bytes);
   uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   asm("" : "+s"(hi));
   return hi ? 0xFFFFFFFFu : (uint32_t)b;
@@ -153,7 +154,7 @@ struct Stage {
 // as 0 through the buffer range check.  K and V parts can be fetched separately.
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
-  const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
+  const int64_t row0 = (int64_t)tile_index_clamped(kt) * kTile;  // never a base before the store
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;  // bytes between tokens
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
@@ -191,7 +192,7 @@ __device__ __forceinline__ void load_tile_k(Stage<MODE, NT>& st, const AttnChunk
 
 template <int MODE, int NT>
 __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk& a, int head, int kt, int tid) {
-  const int64_t row0 = (int64_t)(kt > 0 ? kt : 0) * kTile;  // never a base before the store
+  const int64_t row0 = (int64_t)tile_index_clamped(kt) * kTile;  // never a base before the store
   if constexpr (MODE == 0) {
     const int rstride = a.n_heads * kHeadDim * 2;
     const int64_t off0 = (row0 * a.n_heads + head) * kHeadDim * 2;
