@@ -414,9 +414,9 @@ def main() -> int:
     def step(record: bool):
         if record:
             ev["quant"][0].record(stream)
-        for t0 in range(0, w.seq, w.q_chunk):
-            h3a.h3a_kv_quantize(x["k"][t0:t0 + w.q_chunk], kc, sc[0], token_offset=t0)
-            h3a.h3a_kv_quantize(x["v"][t0:t0 + w.q_chunk], vc, sc[1], token_offset=t0)
+        for t0 in range(0, w.seq, w.q_chunk):  # K and V of each kv_chunk in one launch
+            h3a.h3a_kv_quantize_pair(x["k"][t0:t0 + w.q_chunk], x["v"][t0:t0 + w.q_chunk], kc, vc, sc,
+                                     token_offset=t0)
         if record:
             ev["quant"][1].record(stream)
             ev["kvi8r"][0].record(stream)
@@ -439,6 +439,7 @@ def main() -> int:
     # Timed region: K steps between two device synchronisations.  Attention-kernel
     # launches of the kvi8r pass are bracketed by library-side HIP events.
     kern_ms, kern_n = 0.0, 0
+    side = {k: [0.0, 0] for k in ("rotate_q", "unrotate_o")}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -451,6 +452,10 @@ def main() -> int:
         ms, n = h3a.h3a_timing_collect()
         kern_ms += ms
         kern_n += n
+        for k in side:
+            ms, n = h3a.h3a_timing_collect(k)
+            side[k][0] += ms
+            side[k][1] += n
         log(f"step {i + 1}/{args.steps}: kvi8r {ev['kvi8r'][0].elapsed_time(ev['kvi8r'][1]):.1f} ms, "
             f"exact {ev['exact'][0].elapsed_time(ev['exact'][1]):.1f} ms")
     torch.cuda.synchronize()
@@ -464,6 +469,15 @@ def main() -> int:
     flops_per_launch = f_mode * args.steps / max(kern_n, 1)
     achieved = flops_per_launch / (kern_avg_ms / 1000.0) / 1e12
     quant_bytes = 2.0 * w.seq * w.heads * (256 + 128 + 2)
+    exps = float(w.seq) * w.seq * w.heads  # one exponential per (query, key) pair and head
+    rows_per_step = float(w.seq) * w.heads  # rotated and un-rotated once per query row and head
+    side_json = {}
+    for k, per_row in (("rotate_q", 256 + 256), ("unrotate_o", 512 + 256)):
+        ms_tot, n = side[k]
+        gbs = rows_per_step * args.steps * per_row / (ms_tot / 1000) / 1e9 if ms_tot > 0 else None
+        side_json[k] = {"ms_per_step": round(ms_tot / args.steps, 3), "launches_per_step": n // args.steps,
+                        "bytes_per_row": per_row, "GB_per_s": None if gbs is None else round(gbs, 1),
+                        "frac_of_hbm_peak": None if gbs is None else round(gbs / PEAK_HBM_GBPS, 4)}
     res = {
         "metric": "attention TFLOP/s at 217k tok, 32h x 128d (kvi8r/exact); % fp16 MFMA peak",
         "value": round(tflops, 2),
@@ -483,13 +497,16 @@ def main() -> int:
         "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4),
         "phases_ms": {k: round(v, 3) for k, v in per.items()},
         "modes": {
-            "kvi8r": {"tflops": round(f_mode / (per["kvi8r"] / 1000) / 1e12, 2),
-                      "frac_of_peak": round(f_mode / (per["kvi8r"] / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4)},
-            "exact": {"tflops": round(f_mode / (per["exact"] / 1000) / 1e12, 2),
-                      "frac_of_peak": round(f_mode / (per["exact"] / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4)},
+            m: {"tflops": round(f_mode / (per[m] / 1000) / 1e12, 2),
+                "frac_of_peak": round(f_mode / (per[m] / 1000) / 1e12 / PEAK_FP16_TFLOPS, 4),
+                "exps": exps, "exps_per_s": round(exps / (per[m] / 1000), 1)}
+            for m in ("kvi8r", "exact")
         },
+        "kvi8r_output": "fp16 (H3A_OUT_F16)",
+        **side_json,
         "kv_quantize": {"ms": round(per["quant"], 3), "GB_per_s": round(quant_bytes / (per["quant"] / 1000) / 1e9, 1),
-                        "frac_of_hbm_peak": round(quant_bytes / (per["quant"] / 1000) / 1e9 / PEAK_HBM_GBPS, 4)},
+                        "frac_of_hbm_peak": round(quant_bytes / (per["quant"] / 1000) / 1e9 / PEAK_HBM_GBPS, 4),
+                        "launches": -(-w.seq // w.q_chunk), "call": "h3a_kv_quantize_pair (K and V of a chunk)"},
         "roofline": {"kernel": "attn_fwd_dense_kernel<1, false> (kvi8r, dense)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": measured_traffic("kvi8r"),

@@ -130,6 +130,24 @@ int32_t h3a_kv_quantize_g32(const void* x, int64_t x_token_stride, int64_t n_tok
                             void* scales_f16, void* stream);
 
 /*
+ * h3a_kv_quantize_pair -- h3a_kv_quantize of K and V of one kv_chunk in one
+ * launch: the projection produces a chunk's K and V together [P1 kv_chunk:
+ * the K/V buffers are built chunk by chunk], and one launch over both keeps
+ * the GPU streaming twice as long between launch ramps.
+ *
+ * k, v:            bf16 [n_tokens, n_heads, 128], both with the same
+ *                  x_token_stride (e.g. two slices of a fused QKV buffer).
+ * k_codes, v_codes: int8 [n_heads, s_total, 128] each, distinct buffers.
+ * scales_f16:      fp16 [2, n_heads, s_total]: K scales, then V scales, the
+ *                  layout h3a_attention takes.
+ * Every other argument, the result and the errors are those of two
+ * h3a_kv_quantize calls (bitwise the same codes and scales).
+ */
+int32_t h3a_kv_quantize_pair(const void* k, const void* v, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads,
+                             int32_t head_dim, int64_t token_offset, int64_t s_total, int8_t* k_codes,
+                             int8_t* v_codes, void* scales_f16, void* stream);
+
+/*
  * h3a_attention_workspace_bytes -- bytes of workspace h3a_attention needs.
  * sparse != 0 when a tile_mask will be passed; mode as passed to h3a_attention
  * (including H3A_SOL).  Returns 0 when none is needed or the arguments are
@@ -307,14 +325,20 @@ int32_t h3a_rotate_rows(const void* x_bf16, void* y_f16, int64_t n_rows, void* s
 int32_t h3a_unrotate_rows(const float* x_f32, void* y_bf16, int64_t n_rows, void* stream);
 
 /*
- * Kernel timing for measurement.  While enabled, h3a_attention brackets every
- * launch of its attention kernel with a pair of HIP events recorded on the
- * call's stream.  h3a_timing_collect waits for the recorded events, returns the
- * summed kernel time (ms) and the number of launches since the last collect,
- * and clears the record.  Disabled by default.
+ * Kernel timing for measurement.  While enabled, the attention entry points
+ * bracket every launch of their attention kernel, and of the query rotation and
+ * output un-rotation of the kvi8r stores, with a pair of HIP events recorded on
+ * the call's stream.  h3a_timing_collect_kernel(kind, ...) waits for the events
+ * recorded for that kernel kind, returns their summed time (ms) and the number
+ * of launches since the last collect of that kind, and clears that record;
+ * h3a_timing_collect is the attention kind.  Disabled by default.
  */
+#define H3A_TIMING_ATTENTION 0
+#define H3A_TIMING_ROTATE_Q 1
+#define H3A_TIMING_UNROTATE_O 2
 int32_t h3a_timing_enable(int32_t on);
 int32_t h3a_timing_collect(double* attn_ms, int64_t* attn_launches);
+int32_t h3a_timing_collect_kernel(int32_t kind, double* ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -8,7 +8,7 @@ There is no CPU fallback: if the library is not built, or its ABI version does
 not match, every call raises.
 
 Functions carry the C names: h3a_kv_quantize (+ h3a_kv_quantize_g32, chosen by the
-scales' shape), h3a_attention, h3a_attention_noalloc, h3a_attention_routed, h3a_attention_host_kv
+scales' shape), h3a_kv_quantize_pair, h3a_attention, h3a_attention_noalloc, h3a_attention_routed, h3a_attention_host_kv
 (+ its workspace query),
 h3a_attention_workspace_bytes, h3a_rotate_rows, h3a_unrotate_rows,
 h3a_timing_enable, h3a_timing_collect, h3a_abi_version.
@@ -62,6 +62,8 @@ def _load():
     lib.h3a_last_error.argtypes = []
     lib.h3a_kv_quantize.restype = i32
     lib.h3a_kv_quantize.argtypes = [vp, i64, i64, i32, i32, i64, i64, vp, vp, vp]
+    lib.h3a_kv_quantize_pair.restype = i32
+    lib.h3a_kv_quantize_pair.argtypes = [vp, vp, i64, i64, i32, i32, i64, i64, vp, vp, vp, vp]
     lib.h3a_kv_quantize_g32.restype = i32
     lib.h3a_kv_quantize_g32.argtypes = [vp, i64, i64, i32, i32, i64, i64, vp, vp, vp]
     lib.h3a_attention_workspace_bytes.restype = sz
@@ -85,6 +87,8 @@ def _load():
     lib.h3a_timing_enable.argtypes = [i32]
     lib.h3a_timing_collect.restype = i32
     lib.h3a_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.h3a_timing_collect_kernel.restype = i32
+    lib.h3a_timing_collect_kernel.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     if lib.h3a_abi_version() != ABI_VERSION:
         raise RuntimeError(f"libh3a ABI {lib.h3a_abi_version()} != binding ABI {ABI_VERSION}")
     _lib = lib
@@ -176,6 +180,29 @@ def h3a_kv_quantize(x, codes, scales, token_offset: int = 0, stream=None):
     fn = lib.h3a_kv_quantize_g32 if grouped else lib.h3a_kv_quantize
     _check(fn(_ptr(x), stride, x.shape[0], x.shape[1], x.shape[2], int(token_offset), codes.shape[1], _ptr(codes),
               _ptr(scales), _stream(x, stream)))
+
+
+def h3a_kv_quantize_pair(k, v, k_codes, v_codes, scales, token_offset: int = 0, stream=None):
+    """Quantise one kv_chunk of K and of V (bf16 [n_tokens, n_heads, 128] each, same strides) in one launch into
+    rows [token_offset, token_offset + n_tokens) of a kvi8r store: codes int8 [n_heads, s_total, 128] each and
+    scales fp16 [2, n_heads, s_total] (K, then V).  Same codes and scales as two h3a_kv_quantize calls."""
+    lib = _load()
+    for name, t in (("k", k), ("v", v)):
+        _need(t, name, torch.bfloat16)
+        if t.dim() != 3 or t.stride(2) != 1 or (t.shape[1] > 1 and t.stride(1) != t.shape[2]):
+            raise ValueError(f"{name} must be [n_tokens, n_heads, head_dim] with contiguous (token, head) rows")
+    if k.shape != v.shape or (k.shape[0] > 1 and k.stride(0) != v.stride(0)):
+        raise ValueError("k and v must have the same shape and token stride")
+    _need(k_codes, "k_codes", torch.int8)
+    _need(v_codes, "v_codes", torch.int8)
+    _need(scales, "scales", torch.float16)
+    if not (k_codes.is_contiguous() and v_codes.is_contiguous() and scales.is_contiguous()) or scales.dim() != 3 \
+            or scales.shape[0] != 2 or k_codes.shape != v_codes.shape:
+        raise ValueError("k_codes / v_codes must be contiguous [n_heads, s_total, 128] and scales contiguous "
+                         "[2, n_heads, s_total]")
+    stride = k.stride(0) if k.shape[0] > 1 else k.shape[1] * k.shape[2]
+    _check(lib.h3a_kv_quantize_pair(_ptr(k), _ptr(v), stride, k.shape[0], k.shape[1], k.shape[2], int(token_offset),
+                                    k_codes.shape[1], _ptr(k_codes), _ptr(v_codes), _ptr(scales), _stream(k, stream)))
 
 
 def new_kvi8r_store(s_total: int, n_heads: int, device="cuda", per32: bool = False):
@@ -389,9 +416,12 @@ def h3a_timing_enable(on: bool):
     _check(_load().h3a_timing_enable(int(bool(on))))
 
 
-def h3a_timing_collect():
-    """(summed attention-kernel milliseconds, launches) since the last collect."""
+TIMING_KINDS = {"attention": 0, "rotate_q": 1, "unrotate_o": 2}
+
+
+def h3a_timing_collect(kind: str = "attention"):
+    """(summed kernel milliseconds, launches) of one timed kernel kind since its last collect."""
     lib = _load()
     ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
-    _check(lib.h3a_timing_collect(ctypes.byref(ms), ctypes.byref(n)))
+    _check(lib.h3a_timing_collect_kernel(TIMING_KINDS[kind], ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value

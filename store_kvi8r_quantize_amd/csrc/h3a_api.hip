@@ -131,13 +131,16 @@ bool workspace_layout(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chun
 // ---- kernel timing --------------------------------------------------------------
 std::mutex g_timing_mu;
 bool g_timing_on = false;
-std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events;
+// Recorded event pairs per timed kernel kind (H3A_TIMING_ATTENTION, _ROTATE_Q, _UNROTATE_O).
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events[3];
 
-// A pair of timing events around one attention-kernel launch on `st`: begin()
-// records the start, end() the stop and hands both to the collection list;
-// a pair that never reached end() is destroyed with the guard.
+// A pair of timing events around one kernel launch on `st`: begin() records the
+// start, end() the stop and hands both to the list of its kind; a pair that
+// never reached end() is destroyed with the guard.
 struct LaunchTimer {
+  int kind = H3A_TIMING_ATTENTION;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  explicit LaunchTimer(int k = H3A_TIMING_ATTENTION) : kind(k) {}
   hipError_t begin(hipStream_t st) {
     hipError_t e;
     if ((e = hipEventCreate(&ev0)) != hipSuccess || (e = hipEventCreate(&ev1)) != hipSuccess) return e;
@@ -147,7 +150,7 @@ struct LaunchTimer {
     hipError_t e = hipEventRecord(ev1, st);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    g_events.emplace_back(ev0, ev1);
+    g_events[kind].emplace_back(ev0, ev1);
     ev0 = ev1 = nullptr;
     return hipSuccess;
   }
@@ -361,8 +364,11 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
     hipError_t e;
     if (p.mode != H3A_MODE_EXACT_BF16) {
       uint16_t* qrot = reinterpret_cast<uint16_t*>(p.ws + p.wl.qrot);
+      LaunchTimer rt(H3A_TIMING_ROTATE_Q);
+      if (p.timing && (e = rt.begin(p.st)) != hipSuccess) return hip_fail(e, "timing event");
       if ((e = h3a::launch_rotate_q(p.q + off, qrot, rows * p.n_heads, p.st)) != hipSuccess)
         return hip_fail(e, "rotate_q launch");
+      if (p.timing && (e = rt.end(p.st)) != hipSuccess) return hip_fail(e, "timing event");
       a.q = qrot;
       a.k_scale = p.k_scale;
       a.v_scale = p.v_scale;
@@ -394,17 +400,22 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
       return hip_fail(e, "attn_fwd launch");
     if (p.timing && (e = timer.end(p.st)) != hipSuccess) return hip_fail(e, "timing event");
     if (p.mode != H3A_MODE_EXACT_BF16) {
+      LaunchTimer ut(H3A_TIMING_UNROTATE_O);
+      if (p.timing && (e = ut.begin(p.st)) != hipSuccess) return hip_fail(e, "timing event");
       if ((e = h3a::launch_unrotate_o(reinterpret_cast<const float*>(p.ws + p.wl.orot), p.out + off,
                                       rows * p.n_heads, p.out_f16, p.st)) != hipSuccess)
         return hip_fail(e, "unrotate_o launch");
+      if (p.timing && (e = ut.end(p.st)) != hipSuccess) return hip_fail(e, "timing event");
     }
   }
   return H3A_OK;
 }
 
-// One quantize call; grouped: one scale per 32 values.
-int kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
-                int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16, bool grouped, void* stream) {
+// One quantize call; grouped: one scale per 32 values.  x2 / codes2 / scales2: a
+// second tensor of the same shape quantised in the same launch, or null.
+int kv_quantize(const void* x, const void* x2, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads,
+                int32_t head_dim, int64_t token_offset, int64_t s_total, int8_t* codes, int8_t* codes2,
+                void* scales_f16, void* scales2_f16, bool grouped, void* stream) {
   g_err.clear();
   if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
   if (n_heads < 1) return fail(H3A_EINVAL, "n_heads must be >= 1 (got %d)", n_heads);
@@ -425,12 +436,19 @@ int kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t
     return fail(H3A_EINVAL, "size overflow");
   xb = (xb + (int64_t)n_heads * H3A_HEAD_DIM) * 2;
   int rc;
-  if ((rc = check_buffer(x, (uint64_t)xb, 16, "x")) != H3A_OK) return rc;
-  if ((rc = check_buffer(codes, (uint64_t)cb, 16, "codes")) != H3A_OK) return rc;
-  if ((rc = check_buffer(scales_f16, (uint64_t)sb, grouped ? 8 : 2, "scales")) != H3A_OK) return rc;
-  hipError_t e = h3a::launch_kvi8r_quantize(static_cast<const uint16_t*>(x), x_token_stride, n_tokens, n_heads,
-                                            token_offset, s_total, codes, static_cast<uint16_t*>(scales_f16),
-                                            grouped, static_cast<hipStream_t>(stream));
+  const bool pair = x2 != nullptr;
+  if ((rc = check_buffer(x, (uint64_t)xb, 16, pair ? "k" : "x")) != H3A_OK) return rc;
+  if ((rc = check_buffer(codes, (uint64_t)cb, 16, pair ? "k_codes" : "codes")) != H3A_OK) return rc;
+  if ((rc = check_buffer(scales_f16, (uint64_t)sb * (pair ? 2 : 1), grouped ? 8 : 2, "scales")) != H3A_OK) return rc;
+  if (pair) {
+    if ((rc = check_buffer(x2, (uint64_t)xb, 16, "v")) != H3A_OK) return rc;
+    if ((rc = check_buffer(codes2, (uint64_t)cb, 16, "v_codes")) != H3A_OK) return rc;
+    if (codes2 == codes) return fail(H3A_EINVAL, "k_codes and v_codes must be different buffers");
+  }
+  hipError_t e = h3a::launch_kvi8r_quantize(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x2), x_token_stride, n_tokens, n_heads,
+      token_offset, s_total, codes, codes2, static_cast<uint16_t*>(scales_f16), static_cast<uint16_t*>(scales2_f16),
+      grouped, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3A_OK : hip_fail(e, "kvi8r_quantize launch");
 }
 
@@ -532,15 +550,27 @@ const char* h3a_last_error(void) { return g_err.c_str(); }
 
 int32_t h3a_kv_quantize(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads, int32_t head_dim,
                         int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16, void* stream) {
-  return kv_quantize(x, x_token_stride, n_tokens, n_heads, head_dim, token_offset, s_total, codes, scales_f16, false,
-                     stream);
+  return kv_quantize(x, nullptr, x_token_stride, n_tokens, n_heads, head_dim, token_offset, s_total, codes, nullptr,
+                     scales_f16, nullptr, false, stream);
 }
 
 int32_t h3a_kv_quantize_g32(const void* x, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads,
                             int32_t head_dim, int64_t token_offset, int64_t s_total, int8_t* codes, void* scales_f16,
                             void* stream) {
-  return kv_quantize(x, x_token_stride, n_tokens, n_heads, head_dim, token_offset, s_total, codes, scales_f16, true,
-                     stream);
+  return kv_quantize(x, nullptr, x_token_stride, n_tokens, n_heads, head_dim, token_offset, s_total, codes, nullptr,
+                     scales_f16, nullptr, true, stream);
+}
+
+int32_t h3a_kv_quantize_pair(const void* k, const void* v, int64_t x_token_stride, int64_t n_tokens, int32_t n_heads,
+                             int32_t head_dim, int64_t token_offset, int64_t s_total, int8_t* k_codes,
+                             int8_t* v_codes, void* scales_f16, void* stream) {
+  g_err.clear();
+  if (head_dim != H3A_HEAD_DIM) return fail(H3A_EUNSUPPORTED, "head_dim must be 128 (got %d)", head_dim);
+  if (n_tokens > 0 && (k == nullptr || v == nullptr)) return fail(H3A_EINVAL, "k and v must both be given");
+  void* v_scales = scales_f16 == nullptr ? nullptr
+                                         : static_cast<char*>(scales_f16) + (size_t)s_total * (size_t)n_heads * 2;
+  return kv_quantize(k, v, x_token_stride, n_tokens, n_heads, head_dim, token_offset, s_total, k_codes, v_codes,
+                     scales_f16, v_scales, false, stream);
 }
 
 size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads, int32_t head_dim, int64_t q_chunk,
@@ -792,27 +822,32 @@ int32_t h3a_timing_enable(int32_t on) {
   return H3A_OK;
 }
 
-int32_t h3a_timing_collect(double* attn_ms, int64_t* attn_launches) {
+int32_t h3a_timing_collect_kernel(int32_t kind, double* ms, int64_t* launches) {
   g_err.clear();
+  if (kind < 0 || kind > 2) return fail(H3A_EINVAL, "unknown timing kind %d", kind);
   std::vector<std::pair<hipEvent_t, hipEvent_t>> evs;
   {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    evs.swap(g_events);
+    evs.swap(g_events[kind]);
   }
   double total = 0.0;
   int rc = H3A_OK;
   for (auto& p : evs) {
-    float ms = 0.0f;
+    float t = 0.0f;
     hipError_t e = hipEventSynchronize(p.second);
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.first, p.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, p.first, p.second);
     if (e != hipSuccess && rc == H3A_OK) rc = hip_fail(e, "kernel timing");
-    total += ms;
+    total += t;
     (void)hipEventDestroy(p.first);
     (void)hipEventDestroy(p.second);
   }
-  if (attn_ms) *attn_ms = total;
-  if (attn_launches) *attn_launches = (int64_t)evs.size();
+  if (ms) *ms = total;
+  if (launches) *launches = (int64_t)evs.size();
   return rc;
+}
+
+int32_t h3a_timing_collect(double* attn_ms, int64_t* attn_launches) {
+  return h3a_timing_collect_kernel(H3A_TIMING_ATTENTION, attn_ms, attn_launches);
 }
 
 }  // extern "C"

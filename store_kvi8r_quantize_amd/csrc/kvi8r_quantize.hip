@@ -30,13 +30,23 @@ constexpr int kHeadsPerBlock = 8;
 constexpr int kTokensPerBlock = 64 / kHeadsPerBlock;
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: adding it rounds |x| < 2^22 to an integer, ties to even
 
+// One tensor of a launch: input rows and the store they go to.
+struct QuantTensor {
+  const uint16_t* x;
+  int8_t* codes;
+  uint16_t* scales;
+};
+
+// blockIdx.y selects the tensor: a launch quantises K and V of one kv_chunk together.
 template <bool GROUPED>
-__global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(256) void kvi8r_quantize_kernel(QuantTensor t0, QuantTensor t1,
                                                              int64_t x_token_stride, int64_t n_tokens,
-                                                             int64_t token_offset, int64_t s_total,
-                                                             int8_t* __restrict__ codes,
-                                                             uint16_t* __restrict__ scales, int32_t n_heads,
+                                                             int64_t token_offset, int64_t s_total, int32_t n_heads,
                                                              uint32_t n_head_blocks) {
+  const QuantTensor tt = blockIdx.y == 0 ? t0 : t1;
+  const uint16_t* __restrict__ x = tt.x;
+  int8_t* __restrict__ codes = tt.codes;
+  uint16_t* __restrict__ scales = tt.scales;
   const int lane = threadIdx.x & 63;
   const int sub = lane & 3;
   const int row_in_block = (threadIdx.x >> 6) * 16 + (lane >> 2);
@@ -122,21 +132,23 @@ __global__ __launch_bounds__(256) void kvi8r_quantize_kernel(const uint16_t* __r
 
 }  // namespace
 
-hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int64_t n_tokens,
+hipError_t launch_kvi8r_quantize(const uint16_t* x, const uint16_t* x2, int64_t x_token_stride, int64_t n_tokens,
                                  int32_t n_heads, int64_t token_offset, int64_t s_total, int8_t* codes,
-                                 uint16_t* scales, bool grouped, hipStream_t stream) {
+                                 int8_t* codes2, uint16_t* scales, uint16_t* scales2, bool grouped,
+                                 hipStream_t stream) {
   if (n_tokens == 0) return hipSuccess;
   // head blocks fastest: workgroup b covers head block b % n_head_blocks of token block b / n_head_blocks
   const uint32_t n_head_blocks = (uint32_t)((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock);
   const int64_t n_wg = (n_tokens + kTokensPerBlock - 1) / kTokensPerBlock * n_head_blocks;
   if (n_wg > 0xFFFFFFFFll) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)n_wg);
+  const QuantTensor t0{x, codes, scales}, t1{x2, codes2, scales2};
+  const dim3 grid((unsigned)n_wg, x2 != nullptr ? 2u : 1u);
   if (grouped)
-    hipLaunchKernelGGL(kvi8r_quantize_kernel<true>, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
-                       token_offset, s_total, codes, scales, n_heads, n_head_blocks);
+    hipLaunchKernelGGL(kvi8r_quantize_kernel<true>, grid, dim3(256), 0, stream, t0, t1, x_token_stride, n_tokens,
+                       token_offset, s_total, n_heads, n_head_blocks);
   else
-    hipLaunchKernelGGL(kvi8r_quantize_kernel<false>, grid, dim3(256), 0, stream, x, x_token_stride, n_tokens,
-                       token_offset, s_total, codes, scales, n_heads, n_head_blocks);
+    hipLaunchKernelGGL(kvi8r_quantize_kernel<false>, grid, dim3(256), 0, stream, t0, t1, x_token_stride, n_tokens,
+                       token_offset, s_total, n_heads, n_head_blocks);
   return hipGetLastError();
 }
 

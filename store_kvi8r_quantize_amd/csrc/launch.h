@@ -9,9 +9,11 @@
 namespace h3a {
 
 // grouped: one scale per 32 rotated values, scales [n_heads, s_total, 4]; else one per row [n_heads, s_total].
-hipError_t launch_kvi8r_quantize(const uint16_t* x, int64_t x_token_stride, int64_t n_tokens,
+// x2 / codes2 / scales2: a second tensor quantised in the same launch (K and V of one chunk), or null.
+hipError_t launch_kvi8r_quantize(const uint16_t* x, const uint16_t* x2, int64_t x_token_stride, int64_t n_tokens,
                                  int32_t n_heads, int64_t token_offset, int64_t s_total, int8_t* codes,
-                                 uint16_t* scales, bool grouped, hipStream_t stream);
+                                 int8_t* codes2, uint16_t* scales, uint16_t* scales2, bool grouped,
+                                 hipStream_t stream);
 
 hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
 // f16: write fp16 rows, else bf16.

@@ -231,3 +231,12 @@ def test_out_f16_flag_does_not_change_workspace_sizes():
                 h3a.h3a_attention_workspace_bytes(1024, 1000, 2, 256, mode, sparse) > 0
     assert h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 256, 1 | 0x200) == \
         h3a.h3a_attention_host_kv_workspace_bytes(1024, 1000, 2, 256, 256, 1)
+
+
+def test_quantize_pair_rejects_bad_arguments(lib):
+    assert lib.h3a_kv_quantize_pair(None, None, 256, 64, 2, 96, 0, 64, None, None, None, None) == -2
+    assert lib.h3a_kv_quantize_pair(None, None, 256, 64, 2, 128, 0, 64, None, None, None, None) == -1
+    assert "k and v" in lib.h3a_last_error().decode()
+    assert lib.h3a_kv_quantize_pair(16, 32, 256, 64, 2, 128, 10, 64, None, None, None, None) == -1
+    assert "exceeds" in lib.h3a_last_error().decode()
+    assert lib.h3a_kv_quantize_pair(None, None, 256, 0, 2, 128, 0, 0, None, None, None, None) == 0

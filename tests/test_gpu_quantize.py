@@ -172,3 +172,30 @@ def test_head_counts_off_the_block_size(n_heads, grouped):
     for h in range(n_heads):
         sh = sg[h, off:off + n].reshape(n, 4) if grouped else sg[h, off:off + n]
         assert_quantize_ok(quantize_report(x[:, h], cg[h, off:off + n], sh, group=32 if grouped else 128))
+
+
+@pytest.mark.parametrize("n_heads", [32, 5])
+def test_pair_equals_two_single_calls(n_heads):
+    # K and V of each chunk in one launch: bitwise the codes and scales of one call per tensor, chunk by chunk
+    # (ragged chunks, at a token offset, a partial head block for 5 heads), from slices of a fused QKV buffer.
+    n, off, total = 3000, 40, 3100
+    w = synth.Workload("pair", n, n_heads, 70 + n_heads, 256, 0, k_outliers=True)
+    bits = synth.qkv_bf16(w, ("k", "v"))
+    fused = torch.zeros((n, 3, n_heads, 128), dtype=torch.bfloat16, device="cuda")
+    fused[:, 1], fused[:, 2] = gpu_u16(bits["k"]), gpu_u16(bits["v"])
+    kc = torch.full((n_heads, total, 128), 7, dtype=torch.int8, device="cuda")
+    vc = torch.full((n_heads, total, 128), 7, dtype=torch.int8, device="cuda")
+    sc = torch.full((2, n_heads, total), 5.0, dtype=torch.float16, device="cuda")
+    kc1, vc1, sc1 = kc.clone(), vc.clone(), sc.clone()
+    for t0 in range(0, n, 1024):
+        t1 = min(t0 + 1024, n)
+        h3a.h3a_kv_quantize_pair(fused[t0:t1, 1], fused[t0:t1, 2], kc, vc, sc, token_offset=off + t0)
+        h3a.h3a_kv_quantize(fused[t0:t1, 1], kc1, sc1[0], token_offset=off + t0)
+        h3a.h3a_kv_quantize(fused[t0:t1, 2], vc1, sc1[1], token_offset=off + t0)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc1) and torch.equal(vc, vc1)
+    assert torch.equal(sc.view(torch.int16), sc1.view(torch.int16))
+    assert bool((kc[:, :off] == 7).all()) and bool((sc[:, :, off + n:] == 5.0).all())
+    for h in (0, n_heads - 1):
+        assert_quantize_ok(quantize_report(bits["v"][:, h], vc[h, off:off + n].cpu().numpy(),
+                                           host_u16(sc[1, h, off:off + n])))
