@@ -259,3 +259,30 @@ def test_side_stream_with_binding_workspace(raw_handle):
     side.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+@pytest.mark.parametrize("q_chunk", [192, 64, 320])
+def test_mask_chunks_of_odd_q_tile_counts(mode, q_chunk):
+    # Chunks of 3, 1 and 5 routing q-tiles; q-tile 4 keeps nothing while q-tile 5 keeps about half its
+    # tiles; q-tiles 6 and 7 keep the same tiles; the ragged last KV tile (s_kv = 1000) is kept by every
+    # other q-tile.  All rows against the oracle, and bitwise equal to q_chunk 128 (each row's tile sequence
+    # does not depend on how rows are grouped into chunks).
+    w = synth.Workload("odd-chunks", 1000, 3, 14, q_chunk, 0)
+    bits = synth.qkv_bf16(w)
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    nt = w.n_tiles
+    rng = np.random.default_rng(21)
+    mask = (rng.random((3, nt, nt)) < 0.3).astype(np.uint8)
+    mask[:, 4, :] = 0
+    mask[:, 5, :] = (rng.random((3, nt)) < 0.5)
+    mask[:, 6, :] = mask[:, 7, :]
+    mask[:, :, nt - 1] = 1  # the partial tile is kept everywhere but q-tile 4
+    mask[:, 4, :] = 0
+    store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
+    m = torch.from_numpy(mask).cuda()
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=q_chunk, mask=m)
+    ref = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=128, mask=m)
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert not bool(out[256:320].any())
+    _check(mode, w.heads, HeadSource(w, bits), out, store, lambda h: np.arange(w.seq), mask=mask, tag="odd-chunks")
