@@ -712,14 +712,17 @@ void attn_fwd_sparse_sol_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt, SolArgs
 // SIMD, software-pipelined across the two waves of each SIMD ("ping-pong").
 // Group 0 (waves 0-3) and group 1 (waves 4-7) hold one wave on every SIMD
 // each.  Between two barriers (one period) group 0 runs
-//     QK(i), softmax(i), PV(i), stage(i+1), [barrier], fetch(i+2)
+//     QK(i), stage(i+1), softmax(i), PV(i) + fetch(i+2), [barrier]
 // and group 1 runs
 //     softmax(i-1), PV(i-1), QK(i), [barrier]
 // so each matrix-core phase of one wave meets a vector phase of the other wave
 // on the same SIMD.  Group 0 alone fetches and stages the K/V tiles (it has
 // the shorter chain of dependent work), so group 1 starts its softmax right
-// after the barrier.  Tiles are triple-buffered in LDS: during period i tiles
-// i-1 and i are read while tile i+1 is written.
+// after the barrier.  The fetch of tile i+2 is issued among the PV MFMAs: a
+// wave issuing a burst of buffer loads stalls while the CU's address unit
+// works through them, and between MFMAs that wait costs nothing.  Tiles are
+// triple-buffered in LDS: during period i tiles i-1 and i are read while tile
+// i+1 is written.
 // STATE: the K/V is one block of a longer store ("H3 Streamed Blocks" node
 // page, kv_block row: K/V attended block by block with a log-sum-exp combine).
 // Each thread resumes its rows' running max, row sum and O accumulators from
@@ -806,18 +809,17 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
     int bi = 0;  // buffer of tile i
     for (int i = 0; i + 1 < n; ++i) {  // periods 0 .. n-2
       const int bn = next3(bi);
+      const int nx = i + 2 < n ? i + 2 : n - 1;  // tile i+2; past the end, the last tile again (never staged)
       qk_block<MODE>(rb, lk(bi));
-      __builtin_amdgcn_sched_barrier(0);
-      sm_full(bi);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_block<MODE>(rb, lv(bi));
       __builtin_amdgcn_sched_barrier(0);
       stage(bn);
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      // tile i+2; past the end, reload the last tile (never staged)
-      load_tile<MODE, NS>(st, a, head, i + 2 < n ? i + 2 : n - 1, tid);
+      sm_full(bi);
       __builtin_amdgcn_sched_barrier(0);
+      load_tile<MODE, NS>(st, a, head, nx, tid);
+      pv_block<MODE>(rb, lv(bi));
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
       bi = bn;
     }
     if (n > 0) {  // period n-1
