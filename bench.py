@@ -3,7 +3,7 @@
 
 One step = one pass of the whole path over one batch of synthetic input at
 217088 tokens x 32 heads x 128 dims (q_chunk = kv_chunk = kv_block = 16384):
-  1. build the kvi8r store: h3a_kv_quantize over K and V, one call per kv_chunk;
+  1. build the kvi8r store: h3a_kv_quantize_pair over K and V, one call per kv_chunk;
   2. kvi8r attention: h3a_attention (rotate each query chunk, attention over the
      int8 store dequantised in the loop, un-rotate once);
   3. exact attention: h3a_attention on the bf16 store.
@@ -14,7 +14,11 @@ per-32-value store (kvi8r32) and one GPU's share of an 8-way head split (4 of
 the 32 heads, q_chunk 16384 and 65536) at long217k, and the hard and Sol arms
 of the block-sparse path at sparse64k.
 `value` is the algorithmic attention throughput of the step,
-2 x 4*S*S*H*128 flop over the step's wall time.
+2 x 4*S*S*H*128 flop over the step's wall time.  The store build, the query
+rotation and the output un-rotation are also reported as HBM rates (algorithmic
+bytes per row x rows over time): kv_quantize once over its phase (first launch
+to last, gaps between launches included) and once over the summed kernel
+durations; rotate_q and unrotate_o over their kernel durations.
 
 Prints one JSON line.  Only one GPU is supported; --gpus N with N > 1 exits.
 """
@@ -439,7 +443,7 @@ def main() -> int:
     # Timed region: K steps between two device synchronisations.  Attention-kernel
     # launches of the kvi8r pass are bracketed by library-side HIP events.
     kern_ms, kern_n = 0.0, 0
-    side = {k: [0.0, 0] for k in ("rotate_q", "unrotate_o")}
+    side = {k: [0.0, 0] for k in ("rotate_q", "unrotate_o", "kv_quantize")}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -471,6 +475,9 @@ def main() -> int:
     quant_bytes = 2.0 * w.seq * w.heads * (256 + 128 + 2)
     exps = float(w.seq) * w.seq * w.heads  # one exponential per (query, key) pair and head
     rows_per_step = float(w.seq) * w.heads  # rotated and un-rotated once per query row and head
+    kq_ms = side["kv_quantize"][0]
+    kq_gbs = round(quant_bytes * args.steps / (kq_ms / 1000) / 1e9, 1) if kq_ms > 0 else None
+    kq_frac = round(kq_gbs / PEAK_HBM_GBPS, 4) if kq_gbs else None
     side_json = {}
     for k, per_row in (("rotate_q", 256 + 256), ("unrotate_o", 512 + 256)):
         ms_tot, n = side[k]
@@ -504,9 +511,14 @@ def main() -> int:
         },
         "kvi8r_output": "fp16 (H3A_OUT_F16)",
         **side_json,
+        # phase time (first launch to last, launch gaps included) and the summed kernel durations
         "kv_quantize": {"ms": round(per["quant"], 3), "GB_per_s": round(quant_bytes / (per["quant"] / 1000) / 1e9, 1),
                         "frac_of_hbm_peak": round(quant_bytes / (per["quant"] / 1000) / 1e9 / PEAK_HBM_GBPS, 4),
-                        "launches": -(-w.seq // w.q_chunk), "call": "h3a_kv_quantize_pair (K and V of a chunk)"},
+                        "kernel_ms": round(side["kv_quantize"][0] / args.steps, 3),
+                        "kernel_GB_per_s": kq_gbs, "kernel_frac_of_hbm_peak": kq_frac,
+                        "bytes_per_row": 256 + 128 + 2,
+                        "launches": side["kv_quantize"][1] // args.steps,
+                        "call": "h3a_kv_quantize_pair (K and V of a chunk)"},
         "roofline": {"kernel": "attn_fwd_dense_kernel<1, false> (kvi8r, dense)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_FP16_TFLOPS, 4), "traffic": measured_traffic("kvi8r"),

@@ -327,15 +327,19 @@ int32_t h3a_unrotate_rows(const float* x_f32, void* y_bf16, int64_t n_rows, void
 /*
  * Kernel timing for measurement.  While enabled, the attention entry points
  * bracket every launch of their attention kernel, and of the query rotation and
- * output un-rotation of the kvi8r stores, with a pair of HIP events recorded on
- * the call's stream.  h3a_timing_collect_kernel(kind, ...) waits for the events
- * recorded for that kernel kind, returns their summed time (ms) and the number
- * of launches since the last collect of that kind, and clears that record;
- * h3a_timing_collect is the attention kind.  Disabled by default.
+ * output un-rotation of the kvi8r stores, and the store-build entry points
+ * (h3a_kv_quantize, h3a_kv_quantize_g32, h3a_kv_quantize_pair) their launch,
+ * with a pair of HIP events recorded on the call's stream.
+ * h3a_timing_collect_kernel(kind, ...) waits for the events recorded for that
+ * kernel kind, returns their summed time (ms) and the number of launches since
+ * the last collect of that kind, and clears that record; an unknown kind
+ * returns H3A_EINVAL.  h3a_timing_collect is the attention kind.  Disabled by
+ * default.
  */
 #define H3A_TIMING_ATTENTION 0
 #define H3A_TIMING_ROTATE_Q 1
 #define H3A_TIMING_UNROTATE_O 2
+#define H3A_TIMING_KV_QUANTIZE 3
 int32_t h3a_timing_enable(int32_t on);
 int32_t h3a_timing_collect(double* attn_ms, int64_t* attn_launches);
 int32_t h3a_timing_collect_kernel(int32_t kind, double* ms, int64_t* launches);

@@ -416,7 +416,7 @@ def h3a_timing_enable(on: bool):
     _check(_load().h3a_timing_enable(int(bool(on))))
 
 
-TIMING_KINDS = {"attention": 0, "rotate_q": 1, "unrotate_o": 2}
+TIMING_KINDS = {"attention": 0, "rotate_q": 1, "unrotate_o": 2, "kv_quantize": 3}
 
 
 def h3a_timing_collect(kind: str = "attention"):

@@ -131,8 +131,9 @@ bool workspace_layout(int64_t s_q, int64_t s_kv, int32_t n_heads, int64_t q_chun
 // ---- kernel timing --------------------------------------------------------------
 std::mutex g_timing_mu;
 bool g_timing_on = false;
-// Recorded event pairs per timed kernel kind (H3A_TIMING_ATTENTION, _ROTATE_Q, _UNROTATE_O).
-std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events[3];
+// Recorded event pairs per timed kernel kind (H3A_TIMING_ATTENTION, _ROTATE_Q, _UNROTATE_O, _KV_QUANTIZE).
+constexpr int kTimingKinds = 4;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events[kTimingKinds];
 
 // A pair of timing events around one kernel launch on `st`: begin() records the
 // start, end() the stop and hands both to the list of its kind; a pair that
@@ -445,10 +446,20 @@ int kv_quantize(const void* x, const void* x2, int64_t x_token_stride, int64_t n
     if ((rc = check_buffer(codes2, (uint64_t)cb, 16, "v_codes")) != H3A_OK) return rc;
     if (codes2 == codes) return fail(H3A_EINVAL, "k_codes and v_codes must be different buffers");
   }
-  hipError_t e = h3a::launch_kvi8r_quantize(
-      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x2), x_token_stride, n_tokens, n_heads,
-      token_offset, s_total, codes, codes2, static_cast<uint16_t*>(scales_f16), static_cast<uint16_t*>(scales2_f16),
-      grouped, static_cast<hipStream_t>(stream));
+  bool timing;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    timing = g_timing_on;
+  }
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  LaunchTimer timer(H3A_TIMING_KV_QUANTIZE);
+  hipError_t e = timing ? timer.begin(st) : hipSuccess;
+  if (e == hipSuccess)
+    e = h3a::launch_kvi8r_quantize(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x2), x_token_stride,
+                                   n_tokens, n_heads, token_offset, s_total, codes, codes2,
+                                   static_cast<uint16_t*>(scales_f16), static_cast<uint16_t*>(scales2_f16), grouped,
+                                   st);
+  if (e == hipSuccess && timing) e = timer.end(st);
   return e == hipSuccess ? H3A_OK : hip_fail(e, "kvi8r_quantize launch");
 }
 
@@ -824,7 +835,7 @@ int32_t h3a_timing_enable(int32_t on) {
 
 int32_t h3a_timing_collect_kernel(int32_t kind, double* ms, int64_t* launches) {
   g_err.clear();
-  if (kind < 0 || kind > 2) return fail(H3A_EINVAL, "unknown timing kind %d", kind);
+  if (kind < 0 || kind >= kTimingKinds) return fail(H3A_EINVAL, "unknown timing kind %d", kind);
   std::vector<std::pair<hipEvent_t, hipEvent_t>> evs;
   {
     std::lock_guard<std::mutex> lk(g_timing_mu);

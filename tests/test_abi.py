@@ -240,3 +240,16 @@ def test_quantize_pair_rejects_bad_arguments(lib):
     assert lib.h3a_kv_quantize_pair(16, 32, 256, 64, 2, 128, 10, 64, None, None, None, None) == -1
     assert "exceeds" in lib.h3a_last_error().decode()
     assert lib.h3a_kv_quantize_pair(None, None, 256, 0, 2, 128, 0, 0, None, None, None, None) == 0
+
+
+def test_timing_kinds_match_the_header(lib):
+    src = open(HEADER).read()
+    kinds = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"#define H3A_TIMING_([A-Z_]+) (\d+)", src)}
+    assert kinds == h3a.TIMING_KINDS
+    ms, n = ctypes.c_double(1.0), ctypes.c_int64(7)
+    for kind in kinds.values():  # nothing timed yet: zero launches, no HIP call
+        assert lib.h3a_timing_collect_kernel(kind, ctypes.byref(ms), ctypes.byref(n)) == 0
+        assert (ms.value, n.value) == (0.0, 0)
+    assert lib.h3a_timing_collect_kernel(len(kinds), ctypes.byref(ms), ctypes.byref(n)) == -1
+    assert "timing kind" in lib.h3a_last_error().decode()
+    assert lib.h3a_timing_collect_kernel(-1, ctypes.byref(ms), ctypes.byref(n)) == -1
