@@ -199,3 +199,43 @@ def test_pair_equals_two_single_calls(n_heads):
     for h in (0, n_heads - 1):
         assert_quantize_ok(quantize_report(bits["v"][:, h], vc[h, off:off + n].cpu().numpy(),
                                            host_u16(sc[1, h, off:off + n])))
+
+
+def _mixed_scale_rows(rng) -> np.ndarray:
+    """bf16 bits [64, 128]: four waves of 16 rows.  Wave 0: N(0,1) rows (normal scales, no clamp).
+    Wave 1: N(0,1) rows and one row whose fp16 scale is subnormal and rounded far down (one-hot
+    magnitude 1.4 subnormal steps), so |y/s| reaches ~178 and the code must clamp to 127.  Wave 2:
+    rows scaled so that their scales run through the subnormal range and across the smallest normal.
+    Wave 3: zero rows, a saturating row of each sign and N(0,1) rows."""
+    rows = rng.standard_normal((64, 128)).astype(np.float32)
+    unit = 2.0 ** -24 * 127 * np.sqrt(128.0)  # max|y| of a one-hot row of this magnitude puts s at 1 step
+    hot = np.zeros(128, np.float32)
+    hot[37] = 1.4 * unit
+    rows[20] = hot
+    rows[32:48] *= (np.float32(2.0) ** -np.linspace(8, 26, 16).astype(np.float32))[:, None]
+    rows[48:51] = 0.0
+    rows[51] = 0.0
+    rows[51, 5] = 2.0 ** 28
+    rows[52] = -rows[51]
+    return synth.bf16_bits_from_f32(rows)
+
+
+@pytest.mark.parametrize("grouped", [False, True])
+def test_clamp_decision_in_mixed_waves(grouped):
+    # Codes skip the clamp only when every row of the wave has a normal fp16 scale below the largest;
+    # rows around those limits, mixed in one wave with ordinary rows, must still match the oracle.
+    x = _mixed_scale_rows(np.random.default_rng(21))
+    xg = gpu_u16(x[:, None, :])
+    codes = torch.empty((1, 64, 128), dtype=torch.int8, device="cuda")
+    scales = torch.empty((1, 64, 4) if grouped else (1, 64), dtype=torch.float16, device="cuda")
+    h3a.h3a_kv_quantize(xg, codes, scales)
+    torch.cuda.synchronize()
+    got_c, got_s = codes.cpu().numpy()[0], host_u16(scales)[0]
+    rep = quantize_report(x, got_c, got_s, group=32 if grouped else 128)
+    say("mixed scales", "grouped" if grouped else "per row", rep)
+    assert_quantize_ok(rep)
+    if not grouped:
+        assert got_s[20] == 1 and np.abs(got_c[20].astype(np.int64)).max() == 127  # clamped subnormal-scale row
+        assert (got_s[32:48] < 0x0400).any() and (got_s[32:48] >= 0x0400).any()  # both sides of the smallest normal
+        assert not got_c[48:51].any() and not got_s[48:51].any()
+        assert got_s[51] == 0x7BFF and got_s[52] == 0x7BFF
