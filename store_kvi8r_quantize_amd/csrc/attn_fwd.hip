@@ -486,29 +486,45 @@ __device__ __forceinline__ u32x4 score_bias(const float* lc, int kb, int jg, int
 // packed fp16 adds (pairs, then a tree); exact sums the fp32 p in a tree.  Row
 // sums avoid v_dot2: it runs on the matrix pipeline and stalls next to MFMA.
 // PSEUDO adds each key's log2 multiplicity to its exponent.
+// The exponents, the exponentials and the packing are written as three passes.
+// For the exact store they are also three scheduling regions (all 32 fma, then
+// all 32 exp, then packs and sums), which measured ~1 % faster; in the kvi8r
+// modes the compiler interleaves them, which measured faster there.
 template <int MODE, bool PARTIAL, bool PSEUDO = false>
 __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float sl2, float nm, int n_valid, int g) {
   using Op = Operand<MODE>;
+  constexpr bool kPhased = MODE == 0;
+  float x[32];  // x[16 kb + 4 jg + e]: key 32 kb + 8 jg + 4 g + e
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int jg = 0; jg < 4; ++jg) {
+      const u32x4 cc = score_factors<MODE, PSEUDO>(lc, sl2, kb, jg, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float t = __builtin_fmaf(rb.s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
+        if constexpr (PSEUDO) t += __uint_as_float(score_bias(lc, kb, jg, g)[e]);
+        if constexpr (PARTIAL) t = 32 * kb + 8 * jg + 4 * g + e < n_valid ? t : -__builtin_inff();
+        x[16 * kb + 4 * jg + e] = t;
+      }
+    }
+  if constexpr (kPhased) __builtin_amdgcn_sched_barrier(0);
+  float p[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) p[i] = __builtin_amdgcn_exp2f(x[i]);
+  if constexpr (kPhased) __builtin_amdgcn_sched_barrier(0);
   float gs[8];     // exact: sum of each group of 4
   half2v hs[8];    // kvi8r: packed sum of each group of 4
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int jg = 0; jg < 4; ++jg) {
-      const u32x4 cc = score_factors<MODE, PSEUDO>(lc, sl2, kb, jg, g);
-      float p[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float x = __builtin_fmaf(rb.s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
-        if constexpr (PSEUDO) x += __uint_as_float(score_bias(lc, kb, jg, g)[e]);
-        if constexpr (PARTIAL) x = 32 * kb + 8 * jg + 4 * g + e < n_valid ? x : -__builtin_inff();
-        p[e] = __builtin_amdgcn_exp2f(x);
-      }
-      const uint32_t q01 = Op::pack(p[0], p[1]), q23 = Op::pack(p[2], p[3]);
+      const float* q = p + 16 * kb + 4 * jg;
+      const uint32_t q01 = Op::pack(q[0], q[1]), q23 = Op::pack(q[2], q[3]);
       if constexpr (MODE != 0)
         hs[4 * kb + jg] = __builtin_bit_cast(half2v, q01) + __builtin_bit_cast(half2v, q23);
       else
-        gs[4 * kb + jg] = (p[0] + p[1]) + (p[2] + p[3]);
+        gs[4 * kb + jg] = (q[0] + q[1]) + (q[2] + q[3]);
       rb.pf[kb][jg >> 1][2 * (jg & 1)] = q01;
       rb.pf[kb][jg >> 1][2 * (jg & 1) + 1] = q23;
     }
