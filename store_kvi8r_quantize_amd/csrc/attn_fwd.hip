@@ -30,8 +30,8 @@
 //   * K/V tiles are fetched with buffer loads whose range check zero-fills rows
 //     past the end of the store (no per-row compares), held in registers one
 //     tile ahead, and written to LDS once per workgroup: kvi8r codes become
-//     fp16 by a byte permute under the 0x64 exponent byte and one packed subtract;
-//     V rows then get one packed multiply by their scale.  K stays as exact
+//     fp16 by one SDWA conversion of the sign-extended byte each; V rows then
+//     get one packed multiply by their scale.  K stays as exact
 //     integer codes and each key's scale (times softmax_scale * log2 e) is
 //     applied to that key's fp32 score, which keeps the fp16 rounding of
 //     code * scale out of the scores.  The kvi8r32 store (one scale per 32
@@ -86,27 +86,34 @@ struct Operand<1> {  // kvi8r store: fp16 operands
 template <>
 struct Operand<2> : Operand<1> {};  // kvi8r32 store (one scale per 32 values): fp16 operands
 
-// int8 codes -> fp16.  For u = code ^ 0x80 (= code + 128 as an unsigned byte),
-// the fp16 bit pattern 0x64 << 8 | u is 1024 + u; subtracting 1152 leaves the
-// code exactly.  byte_pair places bytes (0, 1) or (2, 3) of a dword under that
-// exponent.  The helpers return each pair's final bits straight from its half2
-// expression: packing fp16 pairs into a small vector, extracting and bit-casting
-// them back for more fp16 arithmetic was miscompiled (the (2, 3) pair was
-// replaced by the (0, 1) pair) by the ROCm 7.2 device compiler.
-constexpr uint32_t kSelLo = 0x04010400u, kSelHi = 0x04030402u;
-
-__device__ __forceinline__ half2v byte_pair(uint32_t u, uint32_t sel) {
-  return __builtin_bit_cast(half2v, __builtin_amdgcn_perm(0x64646464u, u, sel));
+// int8 codes -> fp16.  code_pair<K> converts bytes (2K, 2K+1) of a dword, as
+// signed codes, into an fp16 pair with two SDWA conversions: v_cvt_f16_i16 on
+// the sign-extended byte (exact, |code| <= 128), the first writing the low half,
+// the second the high half while keeping the low.  That is two instructions a
+// pair; the byte-under-exponent form (a byte permute under 0x64, one packed
+// subtract of 1152, and one xor per four codes to make them unsigned) took
+// 2.25, and the compiler does not form this sequence from C (it shifts each
+// byte down and converts through fp32).  The inline asm only reads and writes
+// the registers it names.  dequant_pair multiplies the pair by a packed scale:
+// fp16(code * scale), rounded once.
+template <int K>
+__device__ __forceinline__ uint32_t code_pair(uint32_t w) {
+  static_assert(K == 0 || K == 1, "a dword holds two byte pairs");
+  uint32_t r;
+  if constexpr (K == 0)
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
+        : "=&v"(r) : "v"(w));
+  else
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+        "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
+        : "=&v"(r) : "v"(w));
+  return r;
 }
 
-__device__ __forceinline__ uint32_t code_pair(uint32_t u, uint32_t sel) {
-  const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  return __builtin_bit_cast(uint32_t, byte_pair(u, sel) - bias);
-}
-
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t u, uint32_t sel, half2v s2) {
-  const half2v bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  return __builtin_bit_cast(uint32_t, (byte_pair(u, sel) - bias) * s2);
+template <int K>
+__device__ __forceinline__ uint32_t dequant_pair(uint32_t w, half2v s2) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, code_pair<K>(w)) * s2);
 }
 
 // Buffer resource over `bytes` bytes from base; loads past them read 0.  Every
@@ -269,20 +276,16 @@ __device__ __forceinline__ void store_tile_k(const Stage<MODE, NT>& st, uint16_t
       c1 = st.k[j][1];
     } else if constexpr (MODE == 1) {
       const u32x4 w = st.k[j][0];
-      const uint32_t u0 = w[0] ^ 0x80808080u, u1 = w[1] ^ 0x80808080u;
-      const uint32_t u2 = w[2] ^ 0x80808080u, u3 = w[3] ^ 0x80808080u;
-      c0 = u32x4{code_pair(u0, kSelLo), code_pair(u0, kSelHi), code_pair(u1, kSelLo), code_pair(u1, kSelHi)};
-      c1 = u32x4{code_pair(u2, kSelLo), code_pair(u2, kSelHi), code_pair(u3, kSelLo), code_pair(u3, kSelHi)};
+      c0 = u32x4{code_pair<0>(w[0]), code_pair<1>(w[0]), code_pair<0>(w[1]), code_pair<1>(w[1])};
+      c1 = u32x4{code_pair<0>(w[2]), code_pair<1>(w[2]), code_pair<0>(w[3]), code_pair<1>(w[3])};
     } else {  // kvi8r32: a key has four scales, so K is dequantised to fp16 here like V
       const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.ks[j]);
       const half2v s2 = {sc, sc};
       const u32x4 w = st.k[j][0];
-      const uint32_t u0 = w[0] ^ 0x80808080u, u1 = w[1] ^ 0x80808080u;
-      const uint32_t u2 = w[2] ^ 0x80808080u, u3 = w[3] ^ 0x80808080u;
-      c0 = u32x4{dequant_pair(u0, kSelLo, s2), dequant_pair(u0, kSelHi, s2), dequant_pair(u1, kSelLo, s2),
-                 dequant_pair(u1, kSelHi, s2)};
-      c1 = u32x4{dequant_pair(u2, kSelLo, s2), dequant_pair(u2, kSelHi, s2), dequant_pair(u3, kSelLo, s2),
-                 dequant_pair(u3, kSelHi, s2)};
+      c0 = u32x4{dequant_pair<0>(w[0], s2), dequant_pair<1>(w[0], s2), dequant_pair<0>(w[1], s2),
+                 dequant_pair<1>(w[1], s2)};
+      c1 = u32x4{dequant_pair<0>(w[2], s2), dequant_pair<1>(w[2], s2), dequant_pair<0>(w[3], s2),
+                 dequant_pair<1>(w[3], s2)};
     }
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16) = c0;
     *reinterpret_cast<u32x4*>(lk + r * kKStride + 16 * d16 + 8) = c1;
@@ -303,9 +306,8 @@ __device__ __forceinline__ void store_tile_v(const Stage<MODE, NT>& st, uint16_t
     } else {
       const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.vs[j]);
       const half2v s2 = {sc, sc};
-      const uint32_t w0 = st.v[j][0] ^ 0x80808080u, w1 = st.v[j][1] ^ 0x80808080u;
-      c = u32x4{dequant_pair(w0, kSelLo, s2), dequant_pair(w0, kSelHi, s2), dequant_pair(w1, kSelLo, s2),
-                dequant_pair(w1, kSelHi, s2)};
+      const uint32_t w0 = st.v[j][0], w1 = st.v[j][1];
+      c = u32x4{dequant_pair<0>(w0, s2), dequant_pair<1>(w0, s2), dequant_pair<0>(w1, s2), dequant_pair<1>(w1, s2)};
     }
     *reinterpret_cast<u32x4*>(lv + r * kVStride + 8 * d8) = c;
   }
