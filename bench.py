@@ -11,8 +11,8 @@ Inputs are resident in HBM before timing.  After the timed steps, extra legs
 (each its own JSON object) time the per-row routed call (exact_av_rows), the
 host-staged K/V call (store in pinned host memory, PCIe-inclusive), the
 per-32-value store (kvi8r32) and one GPU's share of an 8-way head split (4 of
-the 32 heads, q_chunk 16384 and 65536) at long217k, and the hard and Sol arms
-of the block-sparse path at sparse64k.
+the 32 heads, q_chunk 16384 and 65536) at long217k, and the block-sparse path
+at sparse64k: the kvi8r store's hard and Sol arms and the exact store's hard arm.
 `value` is the algorithmic attention throughput of the step,
 2 x 4*S*S*H*128 flop over the step's wall time.  The store build, the query
 rotation and the output un-rotation are also reported as HBM rates (algorithmic
@@ -164,8 +164,9 @@ def cpu_baseline(w, store, seconds: float):
 
 
 def sparse_legs(h3a, dev, reps: int):
-    """kvi8r attention over the 64Q x 64KV tile-masked sparse64k workload (30 % video KV density):
-    the hard arm (dropped tiles left out) and the Sol arm (each dropped tile one pseudo-key)."""
+    """Attention over the 64Q x 64KV tile-masked sparse64k workload (30 % video KV density): kvi8r
+    store, hard arm (dropped tiles left out) and Sol arm (each dropped tile one pseudo-key); and the
+    exact bf16 store, hard arm."""
     import numpy as np
     import torch
 
@@ -179,18 +180,20 @@ def sparse_legs(h3a, dev, reps: int):
     for t0 in range(0, w.seq, w.q_chunk):
         h3a.h3a_kv_quantize(x["k"][t0:t0 + w.q_chunk], kc, sc[0], token_offset=t0)
         h3a.h3a_kv_quantize(x["v"][t0:t0 + w.q_chunk], vc, sc[1], token_offset=t0)
-    out = torch.empty(x["q"].shape, dtype=torch.float16, device=dev)
+    outs = {"kvi8r": torch.empty(x["q"].shape, dtype=torch.float16, device=dev),
+            "exact": torch.empty_like(x["q"])}
+    stores = {"kvi8r": (kc, vc, sc), "exact": (x["k"], x["v"], None)}
     stream = torch.cuda.current_stream(dev)
     # query rows per q-tile and pseudo-keys (dropped tiles) per (head, q-tile)
     rows = np.full(w.n_tiles, 64.0)
     rows[-1] = w.seq - 64 * (w.n_tiles - 1)
     pseudo_flops = float(4.0 * 128 * np.einsum("hq,q->", (mask_np == 0).sum(axis=2).astype(np.float64), rows))
     res = {}
-    for sol in (False, True):
-        ws = torch.empty(max(h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, w.q_chunk, "kvi8r", True,
+    for mode, sol in (("kvi8r", False), ("kvi8r", True), ("exact", False)):
+        ws = torch.empty(max(h3a.h3a_attention_workspace_bytes(w.seq, w.seq, w.heads, w.q_chunk, mode, True,
                                                                sol=sol), 256), dtype=torch.uint8, device=dev)
-        call = lambda: h3a.h3a_attention(x["q"], kc, vc, sc, out, q_chunk=w.q_chunk, mode="kvi8r", tile_mask=mask,
-                                         sol=sol, workspace=ws)
+        call = lambda: h3a.h3a_attention(x["q"], *stores[mode], outs[mode], q_chunk=w.q_chunk, mode=mode,
+                                         tile_mask=mask, sol=sol, workspace=ws)
         call()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -202,14 +205,14 @@ def sparse_legs(h3a, dev, reps: int):
         ms = e0.elapsed_time(e1) / reps
         flops = attention_flops(w, mask_np) + (pseudo_flops if sol else 0.0)
         tflops = flops / (ms / 1000) / 1e12
-        r = {"workload": w.name, "mode": "kvi8r", "arm": "sol" if sol else "hard", "seq": w.seq, "heads": w.heads,
+        r = {"workload": w.name, "mode": mode, "arm": "sol" if sol else "hard", "seq": w.seq, "heads": w.heads,
              "q_chunk": w.q_chunk, "kept_tile_frac": round(float(mask_np.mean()), 4),
              "tflop_algorithmic": round(flops / 1e12, 3), "ms": round(ms, 3), "tflops": round(tflops, 2),
              "frac_of_peak": round(tflops / PEAK_FP16_TFLOPS, 4)}
         if sol:
             r["pseudo_keys_per_row"] = round(float((mask_np == 0).sum(axis=2).mean()), 1)
             r["ms_over_hard"] = round(ms - res["sparse64k"]["ms"], 3)
-        res["sparse64k_sol" if sol else "sparse64k"] = r
+        res["sparse64k_sol" if sol else "sparse64k" if mode == "kvi8r" else "sparse64k_exact"] = r
         del ws
     return res
 
@@ -573,7 +576,8 @@ def main() -> int:
         del x, out_e, ws
         torch.cuda.empty_cache()
         res.update(sparse_legs(h3a, dev, reps=3))
-        log(f"sparse64k: hard {res['sparse64k']['tflops']} TFLOP/s, sol {res['sparse64k_sol']['tflops']} TFLOP/s")
+        log(f"sparse64k: hard {res['sparse64k']['tflops']} TFLOP/s, sol {res['sparse64k_sol']['tflops']} TFLOP/s, "
+            f"exact store {res['sparse64k_exact']['tflops']} TFLOP/s")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(w, (kc, vc, sc), args.cpu_seconds)

@@ -17,7 +17,9 @@
 // MI355X design
 //   * Dense: workgroup = 8 waves x 32 query rows = 256 rows of one head, two
 //     waves per SIMD in a ping-pong (see attn_fwd_dense_kernel).  Sparse:
-//     2 waves x 32 rows = one 64-row routing tile.  Key/value tiles of 64 tokens.
+//     2 waves x 32 rows = one 64-row routing tile; for the exact store, 8 waves
+//     for two routing tiles, half of them only staging (attn_fwd_sparse_pair_kernel).
+//     Key/value tiles of 64 tokens.
 //   * Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_{f16,bf16}: the
 //     query index runs across lanes, keys across the 16 accumulator registers,
 //     so the softmax row sums are in-lane (plus one exchange between lanes l
@@ -731,6 +733,116 @@ void attn_fwd_sparse_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
   attn_fwd_sparse_body<MODE, false>(a, n_qt, n_kt, SolArgs{}, lds_k, lds_v, lds_c);
 }
 
+// Block-sparse kernel, paired form: one workgroup = 8 waves = two 64-row routing
+// q-tiles (2j and 2j+1) of one head.  Waves 0-1 attend q-tile 2j's rows and
+// waves 2-3 q-tile 2j+1's; waves 4-5 stage q-tile 2j's kept tiles and 6-7 those
+// of 2j+1.  Wave w runs on SIMD w % 4, so each SIMD holds one attending and one
+// staging wave, and the staging runs beside the attending wave's matrix-core
+// work instead of in its chain.  Each q-tile has two LDS slots: in period p its
+// attending waves take tile p of its list from slot p % 2 while its staging
+// waves write tile p+1 into the other slot and fetch tile p+2.  One barrier per
+// period; a q-tile whose list is shorter idles for the remaining periods.
+// Each row's arithmetic is that of attn_fwd_sparse_kernel.  Launched for the
+// exact store, where it is ~20 % faster than the one-q-tile kernel; for the
+// kvi8r stores, whose staging is dominated by code conversions, it is ~4 %
+// slower (the vector work per SIMD is the same, and there it sets the pace).
+template <int MODE>
+__global__ __launch_bounds__(512) void attn_fwd_sparse_pair_kernel(AttnChunk a, int32_t n_qt, int32_t n_kt) {
+  constexpr int NT = 128;
+  constexpr int BM = 64;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][2][kKTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][2][kVTileElems];
+  __shared__ __attribute__((aligned(16))) float lds_c[2][2][kTile];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, g = lane >> 5;
+  const int x = (wave >> 1) & 1;  // which q-tile of the pair
+  const bool stager = wave >= 4;
+
+  const int n_pairs = (n_qt + 1) >> 1;
+  int b = blockIdx.x;
+  const int per = (int)gridDim.x >> 3;
+  if (b < per * 8) b = (b & 7) * per + (b >> 3);
+  const int head = b / n_pairs;
+  const int qt0 = 2 * (b - head * n_pairs);
+  const int qt = qt0 + x;
+  const int32_t* cnt = a.counts + (int64_t)head * n_qt;
+  const int n0 = cnt[qt0];
+  const int n1 = qt0 + 1 < n_qt ? cnt[qt0 + 1] : 0;
+  const int n_tiles = x == 0 ? n0 : n1;
+  const int n_per = n0 > n1 ? n0 : n1;
+  const int32_t* list = a.lists + ((int64_t)head * n_qt + (qt < n_qt ? qt : qt0)) * n_kt;
+  const float sl2 = a.scale_log2;
+
+  if (stager) {
+    const int stid = tid - 256 - 128 * x;
+    Stage<MODE, NT> st;
+    if (n_tiles > 0) {
+      load_tile<MODE, NT>(st, a, head, __builtin_amdgcn_readfirstlane(list[0]), stid);
+      store_tile<MODE, NT>(st, lds_k[x][0], lds_v[x][0], lds_c[x][0], sl2, stid);
+    }
+    if (n_tiles > 1) load_tile<MODE, NT>(st, a, head, __builtin_amdgcn_readfirstlane(list[1]), stid);
+    int nxt = n_tiles > 2 ? list[2] : 0;  // read one period ahead of its use
+    __syncthreads();
+    for (int p = 0; p < n_per; ++p) {
+      const int sl = (p + 1) & 1;
+      if (p + 1 < n_tiles) store_tile<MODE, NT>(st, lds_k[x][sl], lds_v[x][sl], lds_c[x][sl], sl2, stid);
+      if (p + 2 < n_tiles) {
+        const int kt = __builtin_amdgcn_readfirstlane(nxt);
+        if (p + 3 < n_tiles) nxt = list[p + 3];
+        load_tile<MODE, NT>(st, a, head, kt, stid);
+      }
+      __syncthreads();
+    }
+  } else {
+    RowBlock rb;
+    rb.row = (int64_t)qt * BM + (wave & 1) * 32 + c;
+    rb.valid = qt < n_qt && rb.row < a.rows;
+    {
+      const uint16_t* qp = a.q + ((rb.valid ? rb.row : 0) * a.n_heads + head) * kHeadDim + 8 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        rb.q[t] = rb.valid ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb.acc[i] = f32x16{};
+    rb.m = -__builtin_inff();
+    rb.l = 0.0f;
+    // Only the last kept tile can be partial (lists are increasing): full
+    // tiles run in the loop, a partial one after it, then idle periods up to
+    // the longer list of the pair.
+    const int last_full = (int)(a.s_kv / kTile);  // tiles with index >= this one are partial
+    const bool tail = n_tiles > 0 && __builtin_amdgcn_readfirstlane(list[n_tiles - 1]) >= last_full;
+    const int n_full = n_tiles - (tail ? 1 : 0);
+    __syncthreads();
+    int p = 0;
+    for (; p < n_full; ++p) {
+      const int sl = p & 1;
+      const uint16_t* lk = lds_k[x][sl] + c * kKStride + 8 * g;
+      const uint16_t* lv = lds_v[x][sl] + v_lane_offset(lane);
+      qk_block<MODE>(rb, lk);
+      __builtin_amdgcn_sched_barrier(0);
+      softmax_block<MODE, false>(rb, lds_c[x][sl], sl2, kTile, g);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_block<MODE>(rb, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    }
+    if (tail) {
+      const int sl = p & 1;
+      const int kt = __builtin_amdgcn_readfirstlane(list[p]);
+      qk_block<MODE>(rb, lds_k[x][sl] + c * kKStride + 8 * g);
+      softmax_block<MODE, true>(rb, lds_c[x][sl], sl2, (int)(a.s_kv - (int64_t)kt * kTile), g);
+      pv_block<MODE>(rb, lds_v[x][sl] + v_lane_offset(lane));
+      __syncthreads();
+      ++p;
+    }
+    for (; p < n_per; ++p) __syncthreads();
+    store_rows<MODE>(rb, a, head, g);
+  }
+}
+
 // The same with the Sol residual: dropped tiles enter as pseudo-keys.
 template <int MODE>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1017,6 +1129,9 @@ hipError_t launch_sparse(const AttnChunk& a, const SolArgs& sa, hipStream_t stre
   if constexpr (SOL)
     hipLaunchKernelGGL((attn_fwd_sparse_sol_kernel<MODE>), dim3((unsigned)n_wg), dim3(128), 0, stream, a, n_qt,
                        n_kt, sa);
+  else if constexpr (MODE == 0)
+    hipLaunchKernelGGL((attn_fwd_sparse_pair_kernel<MODE>), dim3((unsigned)(((int64_t)n_qt + 1) / 2 * a.n_heads)),
+                       dim3(512), 0, stream, a, n_qt, n_kt);
   else
     hipLaunchKernelGGL((attn_fwd_sparse_kernel<MODE>), dim3((unsigned)n_wg), dim3(128), 0, stream, a, n_qt, n_kt);
   return hipGetLastError();
