@@ -236,6 +236,29 @@ __device__ __forceinline__ void load_tile_v(Stage<MODE, NT>& st, const AttnChunk
     const int64_t hrow = (int64_t)head * a.s_kv + row0;
     const auto rv = make_rsrc(static_cast<const int8_t*>(a.v) + hrow * kHeadDim, store_span(a, kt, kHeadDim, kHeadDim));
     const auto rvs = make_rsrc(a.v_scale + hrow * G, store_span(a, kt, 2 * G, 2 * G));
+    // kvi8r, 128 staging threads (the sparse kernels): each thread takes 8
+    // consecutive keys at one 8-dim column, so on a whole tile one 16-byte load
+    // brings its 8 V scales (8 loads before; sparse64k 0.7-1.3 % faster).  The
+    // partial last tile loads them key by key, each range-checked.  The dense
+    // kernel keeps one key per 16 threads and unit: there the change measured
+    // no faster.
+    if constexpr (MODE == 1 && NT == 128) {
+      constexpr int VU = Stage<MODE, NT>::VU;
+      const int r0 = VU * (tid >> 4), d8 = tid & 15;
+#pragma unroll
+      for (int j = 0; j < VU; ++j)
+        st.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, (r0 + j) * kHeadDim + 8 * d8, 0, 0));
+      if (rows_to_end(a.s_kv, kt) >= kTile) {  // whole tile: the 8 keys' scales in one load
+        const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, r0 * 2, 0, 0));
+        st.vs[0] = w[0]; st.vs[1] = w[1]; st.vs[2] = w[2]; st.vs[3] = w[3];
+      } else {  // the partial last tile: key by key, each range-checked
+#pragma unroll
+        for (int j = 0; j < VU; j += 2)
+          st.vs[j >> 1] = __builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + j) * 2, 0, 0) |
+                          (__builtin_amdgcn_raw_buffer_load_b16(rvs, (r0 + j + 1) * 2, 0, 0) << 16);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < Stage<MODE, NT>::VU; ++j) {
       const int r = unit_row<NT, 16>(tid, j), d8 = unit_col<NT, 16>(tid, j);
@@ -302,12 +325,15 @@ __device__ __forceinline__ void store_k_factors(const Stage<MODE, NT>& st, float
 
 template <int MODE, int NT>
 __device__ __forceinline__ void store_v_unit(const Stage<MODE, NT>& st, int j, uint16_t* lv, int tid) {
-  const int r = unit_row<NT, 16>(tid, j), d8 = unit_col<NT, 16>(tid, j);
+  constexpr bool kRun = MODE == 1 && NT == 128;  // 8 consecutive keys per thread, scales packed in pairs
+  const int r = kRun ? Stage<MODE, NT>::VU * (tid >> 4) + j : unit_row<NT, 16>(tid, j);
+  const int d8 = kRun ? (tid & 15) : unit_col<NT, 16>(tid, j);
   u32x4 c;
   if constexpr (MODE == 0) {
     c = st.v[j];
   } else {
-    const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)st.vs[j]);
+    const uint32_t sw = kRun ? ((j & 1) ? st.vs[j >> 1] >> 16 : st.vs[j >> 1]) : st.vs[j];
+    const _Float16 sc = __builtin_bit_cast(_Float16, (uint16_t)sw);
     const half2v s2 = {sc, sc};
     const uint32_t w0 = st.v[j][0], w1 = st.v[j][1];
     c = u32x4{dequant_pair<0>(w0, s2), dequant_pair<1>(w0, s2), dequant_pair<0>(w1, s2), dequant_pair<1>(w1, s2)};
