@@ -90,29 +90,33 @@ struct Operand<2> : Operand<1> {};  // kvi8r32 store (one scale per 32 values): 
 
 // int8 codes -> fp16.  code_pair<K> converts bytes (2K, 2K+1) of a dword, as
 // signed codes, into an fp16 pair with two SDWA conversions: v_cvt_f16_i16 on
-// the sign-extended byte (exact, |code| <= 128), the first writing the low half,
-// the second the high half while keeping the low.  That is two instructions a
-// pair; the byte-under-exponent form (a byte permute under 0x64, one packed
-// subtract of 1152, and one xor per four codes to make them unsigned) took
-// 2.25, and the compiler does not form this sequence from C (it shifts each
-// byte down and converts through fp32).  The inline asm only reads and writes
-// the registers it names.  dequant_pair multiplies the pair by a packed scale:
-// fp16(code * scale), rounded once.
+// the sign-extended byte (exact, |code| <= 128), the first writing the whole
+// dword (low half), the second the high half while keeping the low.  That is
+// two instructions a pair; the byte-under-exponent form (a byte permute under
+// 0x64, one packed subtract of 1152, and one xor per four codes to make them
+// unsigned) took 2.25, and the compiler does not form this sequence from C (it
+// shifts each byte down and converts through fp32).  The first conversion
+// writes a whole dword so that the second, which reads it to keep the low
+// half, does not read a partial (dst_sel) write of the instruction before it.
+// The asm reads and writes only the registers it names; after it the compiler
+// puts one wait state before a vector instruction that reads the result (it
+// cannot see that the last write was a partial one, which needs it).
 template <int K>
 __device__ __forceinline__ uint32_t code_pair(uint32_t w) {
   static_assert(K == 0 || K == 1, "a dword holds two byte pairs");
   uint32_t r;
   if constexpr (K == 0)
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
         "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_1"
         : "=&v"(r) : "v"(w));
   else
-    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_0 dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+    asm("v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
         "v_cvt_f16_i16_sdwa %0, sext(%1) dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:BYTE_3"
         : "=&v"(r) : "v"(w));
   return r;
 }
 
+// A pair of codes times a packed scale: fp16(code * scale), rounded once.
 template <int K>
 __device__ __forceinline__ uint32_t dequant_pair(uint32_t w, half2v s2) {
   return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, code_pair<K>(w)) * s2);
