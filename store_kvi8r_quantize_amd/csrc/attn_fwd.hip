@@ -38,7 +38,11 @@
 //     applied to that key's fp32 score, which keeps the fp16 rounding of
 //     code * scale out of the scores.  The kvi8r32 store (one scale per 32
 //     values, "Low VRAM, low RAM", "What is next") has four scales per key, so
-//     its K is dequantised to fp16 in LDS like V.
+//     its K is dequantised to fp16 in LDS like V.  Its score factor is then the
+//     same for every key, so the rotation folds softmax_scale * log2 e into Q'
+//     (one fp16 rounding, as before) and each QK chain starts its accumulators
+//     at -m (the MFMA C operand): the scores come out as exponents, and the
+//     softmax takes no fma.
 //   * LDS: K and V both [key][dim], rows padded so fragment reads and staging
 //     writes are bank-conflict free; triple-buffered in the dense kernel
 //     (112 KB), one buffer in the sparse one (38 KB, four workgroups per CU).
@@ -423,20 +427,25 @@ struct RowBlock {
   f32x16 acc[4];   // O^T accumulator: dims 32*db + 8*(j/4) + 4g + j%4, this lane's row
   f32x16 s[2];     // S^T of the current tile: key 32*kb + 8*(j/4) + 4g + j%4
   u32x4 pf[2][2];  // packed P of the current tile, B operand of O^T += V^T P^T
+  f32x16 cneg;     // kvi8r32: -m (0 while m is -inf) in every register, where QK starts
   float m, l;      // running max (log2 units) and row sum of this lane's keys
   int64_t row;
   bool valid;
 };
 
+// Scores that start from -m: kvi8r32, except on pseudo-key tiles.
+template <int MODE, bool PSEUDO = false>
+constexpr bool kBiasedScores = MODE == 2 && !PSEUDO;
+
 // lk points at this lane's K row c, dims 8g.. of the current buffer.  The two
-// 32-key chains are interleaved.
-template <int MODE>
+// 32-key chains are interleaved.  CN: the chains start at rb.cneg.
+template <int MODE, bool CN = kBiasedScores<MODE>>
 __device__ __forceinline__ void qk_issue(RowBlock& rb, const uint16_t* lk) {
   using Op = Operand<MODE>;
   u32x4 ka[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) ka[i] = *reinterpret_cast<const u32x4*>(lk + 32 * (i & 1) * kKStride + 16 * (i >> 1));
-  f32x16 s0 = {}, s1 = {};
+  f32x16 s0 = CN ? rb.cneg : f32x16{}, s1 = CN ? rb.cneg : f32x16{};
 #pragma unroll
   for (int i = 0; i < 16; i += 2) {
     s0 = Op::mfma(ka[i], rb.q[i >> 1], s0);
@@ -460,9 +469,9 @@ __device__ __forceinline__ void mfma_read_pattern() {
   __builtin_amdgcn_sched_group_barrier(0x008, kAhead, 0);
 }
 
-template <int MODE>
+template <int MODE, bool CN = kBiasedScores<MODE>>
 __device__ __forceinline__ void qk_block(RowBlock& rb, const uint16_t* lk) {
-  qk_issue<MODE>(rb, lk);
+  qk_issue<MODE, CN>(rb, lk);
   mfma_read_pattern<1>();
 }
 
@@ -550,8 +559,9 @@ __device__ __forceinline__ void pv_block(RowBlock& rb, const uint16_t* lv) {
 }
 
 // Score factors of this lane's keys 32*kb + 8*jg + 4g + {0..3}: key scale *
-// softmax_scale * log2 e (kvi8r, from LDS) or softmax_scale * log2 e (exact,
-// and kvi8r32, whose K is dequantised in LDS).
+// softmax_scale * log2 e (kvi8r, from LDS) or softmax_scale * log2 e (exact;
+// kvi8r32, whose K is dequantised in LDS and whose Q' already carries the
+// factor, takes 1).
 // Pseudo-key tiles (Sol residual) take theirs from LDS in both modes, and also
 // a per-key additive term, log2 of the key's multiplicity, from lc + kTile.
 template <int MODE, bool PSEUDO = false>
@@ -573,9 +583,12 @@ __device__ __forceinline__ u32x4 score_bias(const float* lc, int kb, int jg, int
 // For the exact store they are also three scheduling regions (all 32 fma, then
 // all 32 exp, then packs and sums), which measured ~1 % faster; in the kvi8r
 // modes the compiler interleaves them, which measured faster there.
-template <int MODE, bool PARTIAL, bool PSEUDO = false>
+// Biased scores (kvi8r32) already are s * factor - m for the m the QK started
+// from: p = exp2(s), or exp2(s + nm) with nm the change of m when ADD.
+template <int MODE, bool PARTIAL, bool PSEUDO = false, bool ADD = false>
 __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float sl2, float nm, int n_valid, int g) {
   using Op = Operand<MODE>;
+  constexpr bool kBiased = kBiasedScores<MODE, PSEUDO>;
   constexpr bool kPhased = MODE == 0;
   float x[32];  // x[16 kb + 4 jg + e]: key 32 kb + 8 jg + 4 g + e
 #pragma unroll
@@ -585,7 +598,9 @@ __device__ __forceinline__ float tile_exps(RowBlock& rb, const float* lc, float 
       const u32x4 cc = score_factors<MODE, PSEUDO>(lc, sl2, kb, jg, g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float t = __builtin_fmaf(rb.s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
+        float t;
+        if constexpr (kBiased) t = ADD ? rb.s[kb][4 * jg + e] + nm : rb.s[kb][4 * jg + e];
+        else t = __builtin_fmaf(rb.s[kb][4 * jg + e], __uint_as_float(cc[e]), nm);
         if constexpr (PSEUDO) t += __uint_as_float(score_bias(lc, kb, jg, g)[e]);
         if constexpr (PARTIAL) t = 32 * kb + 8 * jg + 4 * g + e < n_valid ? t : -__builtin_inff();
         x[16 * kb + 4 * jg + e] = t;
@@ -627,7 +642,13 @@ __device__ __forceinline__ float softmax_fast(RowBlock& rb, const float* lc, flo
 template <int MODE, bool PARTIAL, bool PSEUDO = false>
 __device__ __forceinline__ void softmax_finish(RowBlock& rb, float lsum, const float* lc, float sl2, int n_valid,
                                                int g) {
-  if (!(pair_max(lsum) <= kLazyBound)) {
+  constexpr bool kBiased = kBiasedScores<MODE, PSEUDO>;
+  bool redo = !(pair_max(lsum) <= kLazyBound);
+  // Biased scores start from 0 while m is -inf, so the first tile is redone
+  // by this test rather than by an infinite sum.
+  if constexpr (kBiased) redo = redo || rb.m == -__builtin_inff();
+  if (redo) {
+    const float mb = rb.m == -__builtin_inff() ? 0.0f : rb.m;  // the m the biased scores hold
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -637,18 +658,23 @@ __device__ __forceinline__ void softmax_finish(RowBlock& rb, float lsum, const f
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (!PARTIAL || 32 * kb + 8 * jg + 4 * g + e < n_valid) {
-            float x = rb.s[kb][4 * jg + e] * __uint_as_float(cc[e]);
+            float x = kBiased ? rb.s[kb][4 * jg + e] : rb.s[kb][4 * jg + e] * __uint_as_float(cc[e]);
             if constexpr (PSEUDO) x += __uint_as_float(score_bias(lc, kb, jg, g)[e]);
             mx = fmaxf(mx, x);
           }
       }
     mx = pair_max(mx);
+    if constexpr (kBiased) mx += mb;
     const float alpha = __builtin_amdgcn_exp2f(rb.m - mx);
 #pragma unroll
     for (int i = 0; i < 4; ++i) rb.acc[i] *= alpha;
     rb.l *= alpha;
     rb.m = mx;
-    lsum = tile_exps<MODE, PARTIAL, PSEUDO>(rb, lc, sl2, -rb.m, n_valid, g);
+    if constexpr (MODE == 2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) rb.cneg[i] = -mx;
+    if constexpr (kBiased) lsum = tile_exps<MODE, PARTIAL, PSEUDO, true>(rb, lc, sl2, mb - mx, n_valid, g);
+    else lsum = tile_exps<MODE, PARTIAL, PSEUDO>(rb, lc, sl2, -rb.m, n_valid, g);
   }
   rb.l += lsum;
 }
@@ -730,11 +756,12 @@ __device__ __forceinline__ void attn_fwd_sparse_body(const AttnChunk& a, int32_t
 #pragma unroll
   for (int i = 0; i < 4; ++i) rb.acc[i] = f32x16{};
   rb.m = -__builtin_inff();
+  rb.cneg = f32x16{};
   rb.l = 0.0f;
 
   const int n_tiles = a.counts[head * n_qt + qt];
   const int32_t* list = a.lists + ((int64_t)head * n_qt + qt) * n_kt;
-  const float sl2 = a.scale_log2;
+  const float sl2 = MODE == 2 ? 1.0f : a.scale_log2;  // kvi8r32: Q' carries it
   const int last_full = (int)(a.s_kv / kTile);  // tiles with index >= this one are partial
   const uint16_t* lk = lds_k + c * kKStride + 8 * g;
   const uint16_t* lv = lds_v + v_lane_offset(lane);
@@ -795,7 +822,7 @@ __device__ __forceinline__ void attn_fwd_sparse_body(const AttnChunk& a, int32_t
       stage_pseudo_tile<NT>(a, sa, dl + p0, nv, head, n_kt, lds_k, lds_v, lds_c,
                             reinterpret_cast<int32_t*>(lds_c + 2 * kTile), sl2, tid);
       __syncthreads();
-      qk_block<MODE>(rb, lk);
+      qk_block<MODE, false>(rb, lk);
       softmax_block<MODE, true, true>(rb, lds_c, sl2, nv, g);
       pv_block<MODE>(rb, lv);
     }
@@ -852,7 +879,7 @@ __global__ __launch_bounds__(512) void attn_fwd_sparse_pair_kernel(AttnChunk a, 
   const int n_tiles = x == 0 ? n0 : n1;
   const int n_per = n0 > n1 ? n0 : n1;
   const int32_t* list = a.lists + ((int64_t)head * n_qt + (qt < n_qt ? qt : qt0)) * n_kt;
-  const float sl2 = a.scale_log2;
+  const float sl2 = MODE == 2 ? 1.0f : a.scale_log2;  // kvi8r32: Q' carries it
 
   if (stager) {
     const int stid = tid - 256 - 128 * x;
@@ -887,6 +914,7 @@ __global__ __launch_bounds__(512) void attn_fwd_sparse_pair_kernel(AttnChunk a, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) rb.acc[i] = f32x16{};
     rb.m = -__builtin_inff();
+    rb.cneg = f32x16{};
     rb.l = 0.0f;
     // Only the last kept tile can be partial (lists are increasing): full
     // tiles run in the loop, a partial one after it, then idle periods up to
@@ -986,6 +1014,7 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
 #pragma unroll
   for (int i = 0; i < 4; ++i) rb.acc[i] = f32x16{};
   rb.m = -__builtin_inff();
+  rb.cneg = f32x16{};
   rb.l = 0.0f;
   const int64_t state_stride = (int64_t)gridDim.x * 512;      // one array per state register
   const int64_t state_at = (int64_t)b * 512 + tid;             // this thread's slot (logical block b)
@@ -998,11 +1027,14 @@ __global__ __launch_bounds__(512) void attn_fwd_dense_kernel(AttnChunk a, int32_
         for (int j = 0; j < 16; ++j) rb.acc[i][j] = sp[(16 * i + j) * state_stride];
       rb.m = sp[64 * state_stride];
       rb.l = sp[65 * state_stride];
+      if (MODE == 2 && rb.m != -__builtin_inff())
+#pragma unroll
+        for (int i = 0; i < 16; ++i) rb.cneg[i] = -rb.m;
     }
   }
 
   const int n = n_kt;
-  const float sl2 = a.scale_log2;
+  const float sl2 = MODE == 2 ? 1.0f : a.scale_log2;  // kvi8r32: Q' carries it
   const bool tail = n > 0 && (int64_t)n * kTile > a.s_kv;  // the last tile is partial
   const int n_valid_last = n > 0 ? (int)(a.s_kv - (int64_t)(n - 1) * kTile) : 0;
   // Buffer b of tile t is t % 3; callers pass b, kept in scalar registers.

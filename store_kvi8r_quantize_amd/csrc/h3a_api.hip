@@ -68,6 +68,11 @@ int check_buffer(const void* p, uint64_t bytes, unsigned align, const char* name
   return H3A_OK;
 }
 
+// Factor the query rotation applies before rounding: the kvi8r32 attention
+// kernels take softmax_scale * log2 e from Q' (their K is dequantised, so every
+// key has the same score factor); the kvi8r kernels apply it per key.
+float q_post(int32_t mode, float scale_log2) { return mode == H3A_MODE_KVI8R32 ? scale_log2 : 1.0f; }
+
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
   if (a != 0 && b > INT64_MAX / a) return false;
@@ -367,7 +372,8 @@ int attend_rows(const Pass& p, int64_t r0, int64_t r1) {
       uint16_t* qrot = reinterpret_cast<uint16_t*>(p.ws + p.wl.qrot);
       LaunchTimer rt(H3A_TIMING_ROTATE_Q);
       if (p.timing && (e = rt.begin(p.st)) != hipSuccess) return hip_fail(e, "timing event");
-      if ((e = h3a::launch_rotate_q(p.q + off, qrot, rows * p.n_heads, p.st)) != hipSuccess)
+      if ((e = h3a::launch_rotate_q(p.q + off, qrot, rows * p.n_heads, q_post(p.mode, p.scale_log2), p.st)) !=
+          hipSuccess)
         return hip_fail(e, "rotate_q launch");
       if (p.timing && (e = rt.end(p.st)) != hipSuccess) return hip_fail(e, "timing event");
       a.q = qrot;
@@ -750,7 +756,9 @@ int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_h
     a.scale_log2 = p.scale_log2;
     if (mode != H3A_MODE_EXACT_BF16) {
       uint16_t* qrot = reinterpret_cast<uint16_t*>(ws + wl.base.qrot);
-      if (!check(h3a::launch_rotate_q(p.q + off, qrot, rows * n_heads, p.st), "rotate_q launch")) break;
+      if (!check(h3a::launch_rotate_q(p.q + off, qrot, rows * n_heads, q_post(mode, p.scale_log2), p.st),
+                 "rotate_q launch"))
+        break;
       a.q = qrot;
       a.out = ws + wl.base.orot;
     } else {
@@ -810,7 +818,7 @@ int32_t h3a_rotate_rows(const void* x_bf16, void* y_f16, int64_t n_rows, void* s
   int rc;
   if ((rc = check_buffer(x_bf16, (uint64_t)n_rows * 256, 16, "x")) != H3A_OK) return rc;
   if ((rc = check_buffer(y_f16, (uint64_t)n_rows * 256, 16, "y")) != H3A_OK) return rc;
-  hipError_t e = h3a::launch_rotate_q(static_cast<const uint16_t*>(x_bf16), static_cast<uint16_t*>(y_f16), n_rows,
+  hipError_t e = h3a::launch_rotate_q(static_cast<const uint16_t*>(x_bf16), static_cast<uint16_t*>(y_f16), n_rows, 1.0f,
                                       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? H3A_OK : hip_fail(e, "rotate_q launch");
 }

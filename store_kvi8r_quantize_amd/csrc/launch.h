@@ -15,7 +15,9 @@ hipError_t launch_kvi8r_quantize(const uint16_t* x, const uint16_t* x2, int64_t 
                                  int8_t* codes2, uint16_t* scales, uint16_t* scales2, bool grouped,
                                  hipStream_t stream);
 
-hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, hipStream_t stream);
+// post: a factor applied before the rounding to fp16 (1, or softmax_scale * log2 e
+// for the kvi8r32 store's attention).
+hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, float post, hipStream_t stream);
 // f16: write fp16 rows, else bf16.
 hipError_t launch_unrotate_o(const float* x, uint16_t* y, int64_t n_rows, bool f16, hipStream_t stream);
 

@@ -5,7 +5,9 @@
 // transpose once).  The basis is symmetric, so both directions are y = x H.
 //
 // Same lane layout as kvi8r_quantize: 4 lanes per 128-value row, 16 rows per
-// wave.  Both kernels are HBM-bound streams: rotate reads 256 B and writes 256 B
+// wave.  rotate_q multiplies each value by post before its one rounding to
+// fp16: 1, or softmax_scale * log2 e for the kvi8r32 store, whose attention
+// then needs no per-score factor.  Both kernels are HBM-bound streams: rotate reads 256 B and writes 256 B
 // per row; unrotate reads 512 B and writes 256 B per row (fp16 or bf16).
 #include "h3a_device.h"
 #include "launch.h"
@@ -15,11 +17,12 @@ namespace h3a {
 namespace {
 
 __global__ __launch_bounds__(256) void rotate_q_kernel(const uint16_t* __restrict__ x,
-                                                       uint16_t* __restrict__ y, int64_t n_rows) {
+                                                       uint16_t* __restrict__ y, int64_t n_rows, float post) {
   const int lane = threadIdx.x & 63;
   const int sub = lane & 3;
   const int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 6) * 16 + (lane >> 2);
   if (row >= n_rows) return;  // whole quads leave together: DPP partners stay active
+  const float cs = kInvSqrt128f * post;  // post = 1 leaves 1/sqrt(128) unchanged
   const uint16_t* src = x + row * kHeadDim;
   float v[32];
 #pragma unroll
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(256) void rotate_q_kernel(const uint16_t* __restric
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      w[i] = pack_f16x2(v[8 * k + 2 * i] * kInvSqrt128f, v[8 * k + 2 * i + 1] * kInvSqrt128f);
+      w[i] = pack_f16x2(v[8 * k + 2 * i] * cs, v[8 * k + 2 * i + 1] * cs);
     *reinterpret_cast<u32x4*>(dst + 32 * k + 8 * sub) = w;
   }
 }
@@ -81,10 +84,10 @@ __global__ __launch_bounds__(256) void unrotate_o_kernel(const float* __restrict
 
 }  // namespace
 
-hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, hipStream_t stream) {
+hipError_t launch_rotate_q(const uint16_t* x, uint16_t* y, int64_t n_rows, float post, hipStream_t stream) {
   if (n_rows == 0) return hipSuccess;
   hipLaunchKernelGGL(rotate_q_kernel, dim3((unsigned)((n_rows + 63) / 64)), dim3(256), 0, stream, x, y,
-                     n_rows);
+                     n_rows, post);
   return hipGetLastError();
 }
 
