@@ -73,6 +73,14 @@ int check_buffer(const void* p, uint64_t bytes, unsigned align, const char* name
 // key has the same score factor); the kvi8r kernels apply it per key.
 float q_post(int32_t mode, float scale_log2) { return mode == H3A_MODE_KVI8R32 ? scale_log2 : 1.0f; }
 
+// kvi8r32 multiplies the fp16 query by softmax_scale * log2 e: at most 1, so
+// that the product cannot leave the fp16 range of the rotated query itself.
+int check_mode_scale(int32_t mode, float softmax_scale) {
+  if (mode == H3A_MODE_KVI8R32 && softmax_scale * 1.4426950408889634f > 1.0f)
+    return fail(H3A_EINVAL, "H3A_MODE_KVI8R32 takes softmax_scale <= ln 2 (got %g)", (double)softmax_scale);
+  return H3A_OK;
+}
+
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
   if (a != 0 && b > INT64_MAX / a) return false;
@@ -512,6 +520,7 @@ int attention_call(const void* q, const void* k_store, const void* v_store, cons
   if (sol && s_kv > h3a::kSolMaxKv) return fail(H3A_EINVAL, "H3A_SOL supports s_kv up to 2^30 - 64");
   int rc;
   if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
+  if ((rc = check_mode_scale(mode, softmax_scale)) != H3A_OK) return rc;
   const bool sparse = tile_mask != nullptr;
   if (sparse && q_chunk % H3A_TILE != 0)
     return fail(H3A_EINVAL, "q_chunk must be a multiple of 64 with a tile_mask (got %lld)", (long long)q_chunk);
@@ -690,6 +699,7 @@ int32_t h3a_attention_host_kv(const void* q, const void* k_host, const void* v_h
     return fail(H3A_EINVAL, "H3A_OUT_F16 applies to the kvi8r stores; the exact store's output is bf16");
   int rc;
   if ((rc = check_shapes(s_q, s_kv, n_heads, q_chunk, kv_block, softmax_scale)) != H3A_OK) return rc;
+  if ((rc = check_mode_scale(mode, softmax_scale)) != H3A_OK) return rc;
   if (mode != H3A_MODE_EXACT_BF16 && scales_host == nullptr && s_kv > 0)
     return fail(H3A_EINVAL, "kvi8r modes need scales");
   if (mode == H3A_MODE_EXACT_BF16 && scales_host != nullptr) return fail(H3A_EINVAL, "exact mode takes no scales");

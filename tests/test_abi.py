@@ -75,6 +75,8 @@ def _attn(lib, **kw):
     (dict(mode=0x200 | 0), -1, "H3A_OUT_F16"),
     (dict(mode=0x200 | 0x100 | 0, mask=1), -1, "H3A_OUT_F16"),
     (dict(mode=0x100 | 1, mask=1, scales=16, s_kv=(1 << 30) - 63), -1, "2^30 - 64"),
+    (dict(mode=2, scales=16, scale=0.7), -1, "softmax_scale <= ln 2"),
+    (dict(mode=0x200 | 2, scales=16, scale=2.0), -1, "softmax_scale <= ln 2"),
 ])
 def test_attention_rejects_bad_arguments(lib, kw, status, msg):
     assert _attn(lib, **kw) == status
@@ -155,6 +157,7 @@ def test_quantize_g32_rejects_bad_arguments(lib):
     (dict(mode=0, scales=16), -1, "no scales"),
     (dict(kv_block=100), -1, "kv_block"),
     (dict(q_chunk=0), -1, "q_chunk"),
+    (dict(mode=2, scale=0.7), -1, "softmax_scale <= ln 2"),
 ])
 def test_host_kv_rejects_bad_arguments(lib, kw, status, msg):
     a = dict(s_q=1024, s_kv=1024, n_heads=2, head_dim=128, scale=0.088, q_chunk=256, kv_block=256, mode=1, scales=16)
