@@ -180,7 +180,8 @@ size_t h3a_attention_workspace_bytes(int64_t s_q, int64_t s_kv, int32_t n_heads,
  *   Each K and V row is dequantised group by group (code * group scale,
  *   rounded to fp16) before the fp16 matrix-core products.  The rotated query
  *   is multiplied by softmax_scale * log2(e) before its one rounding to fp16,
- *   so this mode takes softmax_scale <= ln 2 (larger is H3A_EINVAL).
+ *   so this mode takes softmax_scale * log2(e) <= 1 in fp32, i.e. softmax_scale
+ *   up to ln 2 (larger is H3A_EINVAL).
  *
  * q:          bf16 [s_q, n_heads, 128], 16-byte aligned.
  * out:        bf16 [s_q, n_heads, 128] (fp16 with H3A_OUT_F16), 16-byte

@@ -77,7 +77,8 @@ float q_post(int32_t mode, float scale_log2) { return mode == H3A_MODE_KVI8R32 ?
 // that the product cannot leave the fp16 range of the rotated query itself.
 int check_mode_scale(int32_t mode, float softmax_scale) {
   if (mode == H3A_MODE_KVI8R32 && softmax_scale * 1.4426950408889634f > 1.0f)
-    return fail(H3A_EINVAL, "H3A_MODE_KVI8R32 takes softmax_scale <= ln 2 (got %g)", (double)softmax_scale);
+    return fail(H3A_EINVAL, "H3A_MODE_KVI8R32 takes softmax_scale <= ln 2 (softmax_scale * log2 e <= 1; got %g)",
+                (double)softmax_scale);
   return H3A_OK;
 }
 
