@@ -286,3 +286,26 @@ def test_mask_chunks_of_odd_q_tile_counts(mode, q_chunk):
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
     assert not bool(out[256:320].any())
     _check(mode, w.heads, HeadSource(w, bits), out, store, lambda h: np.arange(w.seq), mask=mask, tag="odd-chunks")
+
+
+@pytest.mark.parametrize("mode", ["exact", "kvi8r"])
+def test_mask_lists_of_one_tile_and_the_partial_tile_alone(mode):
+    # 1000 keys: 15 whole tiles and a partial 16th (40 keys).  q-tile 0 keeps only the partial tile (no whole
+    # tile before it), q-tile 1 only tile 0, q-tile 2 tile 0 and the partial one, q-tile 3 nothing, q-tile 4
+    # every tile; the exact store's paired kernel then runs pairs of unequal list lengths with the partial tile
+    # in one list of the pair only.  All rows against the oracle.
+    w = synth.Workload("short-lists", 1000, 2, 15, 256, 0)
+    bits = synth.qkv_bf16(w)
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    nt = w.n_tiles
+    mask = np.zeros((2, nt, nt), dtype=np.uint8)
+    mask[:, 0, nt - 1] = 1
+    mask[:, 1, 0] = 1
+    mask[:, 2, [0, nt - 1]] = 1
+    mask[:, 4, :] = 1
+    rng = np.random.default_rng(5)
+    mask[:, 5:, :] = (rng.random((2, nt - 5, nt)) < 0.3)
+    store = build_store(g["k"], g["v"]) if mode == "kvi8r" else None
+    out = _run(mode, g["q"], g["k"], g["v"], store, q_chunk=256, mask=torch.from_numpy(mask).cuda())
+    assert not bool(out[192:256].any())
+    _check(mode, w.heads, HeadSource(w, bits), out, store, lambda h: np.arange(w.seq), mask=mask, tag="short-lists")

@@ -149,6 +149,36 @@ def test_all_ones_mask_equals_dense_bitwise_and_sol_matches_oracle():
     _check_rows(lambda h: bits["q"][:, h], store, out, range(2), lambda h: np.arange(w.seq), "sol32", sol_ref)
 
 
+@pytest.mark.parametrize("sol", [False, True])
+def test_short_lists_and_the_partial_tile_alone(sol):
+    # Scores that start from -m: q-tile 0 keeps only the partial last tile (its first tile is partial),
+    # q-tile 1 only tile 0, q-tile 2 tile 0 and the partial one, q-tile 3 nothing, q-tile 4 everything;
+    # the hard arm and the Sol arm (dropped tiles as pseudo-keys after the kept ones), all rows.
+    w = synth.Workload("short32", 1000, 2, 15, 256, 0)
+    bits = synth.qkv_bf16(w)
+    g = {t: gpu_u16(bits[t]) for t in bits}
+    store = _store32(g["k"], g["v"])
+    nt = w.n_tiles
+    mask = np.zeros((2, nt, nt), dtype=np.uint8)
+    mask[:, 0, nt - 1] = 1
+    mask[:, 1, 0] = 1
+    mask[:, 2, [0, nt - 1]] = 1
+    mask[:, 4, :] = 1
+    rng = np.random.default_rng(5)
+    mask[:, 5:, :] = (rng.random((2, nt - 5, nt)) < 0.3)
+    out = _attend(g["q"], store, 256, mask=torch.from_numpy(mask).cuda(), sol=sol)
+    if not sol:
+        assert not bool(out[192:256].any())
+
+    def ref(h, rows, q, kc, ks, vc, vs):
+        if sol:
+            return oracle.kvi8r_sol_attention(q, kc, ks, vc, vs, SCALE, rows, mask[h])
+        keep = oracle.expand_tile_mask(mask[h], rows, kc.shape[0])
+        return oracle.kvi8r_attention(q, kc, ks, vc, vs, SCALE, keep)
+    _check_rows(lambda h: bits["q"][:, h], store, out, range(2), lambda h: np.arange(w.seq),
+                "short32-sol" if sol else "short32", ref)
+
+
 def test_finer_scales_land_closer_to_unquantised_attention():
     # outlier keys (4 channels x20): the per-row scale is set by the outliers' groups
     w = synth.WORKLOADS["outlier16k"]
